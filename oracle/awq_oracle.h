@@ -1,0 +1,98 @@
+/*
+ * awq_oracle.h -- CPU oracle for the AWQ per-layer activation-aware scale search.
+ *
+ * TEST INFRASTRUCTURE ONLY. This library is the plain, slow, obviously correct
+ * statement of what the GPU library computes. Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it. It shares no code,
+ * header, table or helper with the HIP library, and the product path never
+ * calls it.
+ *
+ * Sources (web pages on AWQ; cited by page title and section):
+ *   [G]  "AWQ (activation-aware weight quantization)", pigeon guide:
+ *        sections "How it works", "The code, line by line", "Source code".
+ *   [W]  "AWQ > Worked Example: Tracing AWQ Through a Two-Channel Layer".
+ *   [N]  "GPTQ and AWQ weight quantisation" notebook: sections
+ *        "Per-group symmetric int4 (RTN)", "Output MSE vs bit width", "Storage math".
+ *   [C]  "AWQ vs GPTQ Quantization Architectures Compared": sections
+ *        "The shared problem: one layer, sixteen levels",
+ *        "GPTQ: compensate the error you just made" (group_params / rtn listing),
+ *        "AWQ: move the error away from what matters", "What lands on disk".
+ *
+ * Conventions: all pointers are host pointers to contiguous row-major arrays.
+ * W is (out, in), X is (tokens, in); both are given as fp32 arrays holding the
+ * exact values of the stored fp32/fp16/bf16 inputs. Floating point: the
+ * activation statistics, the s-table powers and the output error are fp64;
+ * the group quantizer is fp32 in a fixed operation order with
+ * round-half-to-even; the library is built with -ffp-contract=off.
+ *
+ * Status codes (same numbering as the GPU library, written out separately):
+ *   0 ok, -1 invalid argument, -4 no finite candidate error.
+ */
+#ifndef AWQ_ORACLE_H
+#define AWQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { AWQ_REF_SYM = 0, AWQ_REF_ASYM = 1 };
+
+/* Per-channel mean activation magnitude plus the 1e-8 guard ([G] "How it works"
+ * step 1 and the first line of the awq() listing). Sum order: fp64, sequential
+ * within consecutive 64-token chunks, then the chunk sums in ascending order.
+ * xmag: fp32[in]. */
+void awq_ref_act_stats(const float *X, int64_t tokens, int64_t in, float *xmag);
+
+/* Candidate scales for alpha_k = k/grid, k = 0..grid ([G] "How it works" step 2
+ * and the centring by sqrt(max*min) described in "The code, line by line").
+ * s_table: fp32[(grid+1) * in], row k = candidate k. Returns 0 or -1. */
+int awq_ref_s_table(const float *xmag, int64_t in, int grid, float *s_table);
+
+/* Round-to-nearest group quantizer on one group of g already-scaled values v
+ * (fp32 op order; [N] "Per-group symmetric int4 (RTN)" and the n-bit variant;
+ * [C] group_params / rtn). Outputs: code[i] (stored unsigned code: sym stores
+ * q + 2^(bits-1)), *scale, *zero (sym: 2^(bits-1)), what[i] = dequantized value.
+ * Returns 0 or -1. */
+int awq_ref_quant_group(const float *v, int64_t g, int bits, int mode,
+                        int32_t *code, float *scale, int32_t *zero, float *what);
+
+/* Fake-quantized weight Q(W diag(s)) / s for the whole matrix, fp64 output
+ * ([G] "The code, line by line": scale columns, RTN, divide by s again).
+ * wq: fp64[out*in]. Returns 0 or -1. */
+int awq_ref_fake_quant(const float *W, int64_t out, int64_t in, const float *s,
+                       int bits, int group, int mode, double *wq);
+
+/* Mean squared output error mean((X Wq^T - X W^T)^2) over tokens*out, fp64
+ * ([G] "How it works" step 3; [C] "The shared problem"). wq: fp64[out*in].
+ * nthreads <= 0 means the OpenMP default. Rows are combined in ascending order,
+ * so the value does not depend on the thread count. */
+double awq_ref_output_mse(const float *W, const double *wq, const float *X,
+                          int64_t out, int64_t in, int64_t tokens, int nthreads);
+
+/* The alpha-grid search ([G] "Source code" awq() listing): for each candidate
+ * k: s-table row, fake quantization, output MSE; keep the first strict minimum.
+ * Outputs mse[grid+1], *best (-1 if no candidate error is finite) and
+ * s_best[in] (row `best` of the s-table; all ones when best = -1).
+ * Returns 0, -1, or -4 when best = -1. */
+int awq_ref_search(const float *W, const float *X, int64_t out, int64_t in,
+                   int64_t tokens, const float *xmag, int bits, int group,
+                   int grid, int mode, double *mse, int32_t *best,
+                   float *s_best, int nthreads);
+
+/* Final quantization of W diag(s) and packing ([C] "What lands on disk" for
+ * what is stored; the layout is this library's own):
+ *   qweight: uint32[out][in*bits/32 rounded up]; code i of a row sits at bit
+ *            offset i*bits of that row's little-endian bit stream, each row
+ *            starting on a word boundary;
+ *   scales:  fp32[out][in/group];  zeros: uint8[out][in/group].
+ * Returns 0 or -1. */
+int awq_ref_quantize_pack(const float *W, int64_t out, int64_t in, const float *s,
+                          int bits, int group, int mode, uint32_t *qweight,
+                          float *scales, uint8_t *zeros);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,138 @@
+"""ctypes binding of the CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this module. It takes and returns numpy arrays; W and X are passed as fp32
+arrays holding the exact values of the stored inputs.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+# AWQ_ORACLE_LIB points at another build of this same source; the mutation test
+# uses it to load copies with a planted mistake and check that the pins fail.
+LIB_PATH = os.environ.get("AWQ_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
+
+SYM, ASYM = 0, 1
+_MODES = {"sym": SYM, "asym": ASYM, SYM: SYM, ASYM: ASYM}
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build  # noqa: F401  (package-relative when imported as oracle.oracle)
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+    f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+    u32p = np.ctypeslib.ndpointer(np.uint32, flags="C_CONTIGUOUS")
+    u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+    i64, cint = ctypes.c_int64, ctypes.c_int
+    lib.awq_ref_act_stats.argtypes = [f32p, i64, i64, f32p]
+    lib.awq_ref_act_stats.restype = None
+    lib.awq_ref_s_table.argtypes = [f32p, i64, cint, f32p]
+    lib.awq_ref_s_table.restype = cint
+    lib.awq_ref_quant_group.argtypes = [f32p, i64, cint, cint, i32p, ctypes.POINTER(ctypes.c_float),
+                                        ctypes.POINTER(ctypes.c_int32), f32p]
+    lib.awq_ref_quant_group.restype = cint
+    lib.awq_ref_fake_quant.argtypes = [f32p, i64, i64, f32p, cint, cint, cint, f64p]
+    lib.awq_ref_fake_quant.restype = cint
+    lib.awq_ref_output_mse.argtypes = [f32p, f64p, f32p, i64, i64, i64, cint]
+    lib.awq_ref_output_mse.restype = ctypes.c_double
+    lib.awq_ref_search.argtypes = [f32p, f32p, i64, i64, i64, f32p, cint, cint, cint, cint,
+                                   f64p, ctypes.POINTER(ctypes.c_int32), f32p, cint]
+    lib.awq_ref_search.restype = cint
+    lib.awq_ref_quantize_pack.argtypes = [f32p, i64, i64, f32p, cint, cint, cint, u32p, f32p, u8p]
+    lib.awq_ref_quantize_pack.restype = cint
+    _lib = lib
+    return lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def act_stats(X):
+    X = _f32(X)
+    T, n_in = X.shape
+    xmag = np.empty(n_in, np.float32)
+    _load().awq_ref_act_stats(X, T, n_in, xmag)
+    return xmag
+
+
+def s_table(xmag, grid):
+    xmag = _f32(xmag)
+    out = np.empty((grid + 1, xmag.shape[0]), np.float32)
+    st = _load().awq_ref_s_table(xmag, xmag.shape[0], grid, out)
+    if st != 0:
+        raise ValueError(f"awq_ref_s_table status {st}")
+    return out
+
+
+def quant_group(v, bits, mode):
+    """Returns (codes int32[g], scale float, zero int, dequantized float32[g])."""
+    v = _f32(v)
+    g = v.shape[0]
+    code = np.empty(g, np.int32)
+    what = np.empty(g, np.float32)
+    scale = ctypes.c_float()
+    zero = ctypes.c_int32()
+    st = _load().awq_ref_quant_group(v, g, bits, _MODES[mode], code, ctypes.byref(scale),
+                                     ctypes.byref(zero), what)
+    if st != 0:
+        raise ValueError(f"awq_ref_quant_group status {st}")
+    return code, np.float32(scale.value), int(zero.value), what
+
+
+def fake_quant(W, s, bits, group, mode):
+    W = _f32(W)
+    out, n_in = W.shape
+    wq = np.empty((out, n_in), np.float64)
+    st = _load().awq_ref_fake_quant(W, out, n_in, _f32(s), bits, group, _MODES[mode], wq)
+    if st != 0:
+        raise ValueError(f"awq_ref_fake_quant status {st}")
+    return wq
+
+
+def output_mse(W, wq, X, nthreads=0):
+    W, X = _f32(W), _f32(X)
+    wq = np.ascontiguousarray(wq, dtype=np.float64)
+    out, n_in = W.shape
+    return float(_load().awq_ref_output_mse(W, wq, X, out, n_in, X.shape[0], nthreads))
+
+
+def search(W, X, xmag, bits, group, grid, mode, nthreads=0):
+    """Returns (mse float64[grid+1], best int, s_best float32[in], status)."""
+    W, X, xmag = _f32(W), _f32(X), _f32(xmag)
+    out, n_in = W.shape
+    mse = np.empty(grid + 1, np.float64)
+    s_best = np.empty(n_in, np.float32)
+    best = ctypes.c_int32()
+    st = _load().awq_ref_search(W, X, out, n_in, X.shape[0], xmag, bits, group, grid,
+                                _MODES[mode], mse, ctypes.byref(best), s_best, nthreads)
+    if st not in (0, -4):
+        raise ValueError(f"awq_ref_search status {st}")
+    return mse, int(best.value), s_best, st
+
+
+def words_per_row(n_in, bits):
+    return (n_in * bits + 31) // 32
+
+
+def quantize_pack(W, s, bits, group, mode):
+    """Returns (qweight uint32[out][words], scales float32[out][in/group], zeros uint8[...])."""
+    W = _f32(W)
+    out, n_in = W.shape
+    q = np.empty((out, words_per_row(n_in, bits)), np.uint32)
+    sc = np.empty((out, n_in // group), np.float32)
+    z = np.empty((out, n_in // group), np.uint8)
+    st = _load().awq_ref_quantize_pack(W, out, n_in, _f32(s), bits, group, _MODES[mode], q, sc, z)
+    if st != 0:
+        raise ValueError(f"awq_ref_quantize_pack status {st}")
+    return q, sc, z

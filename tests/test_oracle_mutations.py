@@ -1,0 +1,55 @@
+"""Planted mistakes in the CPU oracle must make its pins fail (CPU only).
+
+Each case copies the oracle source, plants one plausible mistake (a dropped
+term, a wrong sign, index, constant or rounding rule), builds the copy with
+gcc and runs the pin tests against it in a subprocess. A case that still
+passes every pin would mean the pins cannot see that part of the oracle.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "awq_oracle.c")
+
+MUTATIONS = [
+ ("stats drop guard", "xmag[j] = (float)(mean + 1e-8);", "xmag[j] = (float)(mean);"),
+ ("stats T-1", "double mean = total / (double)tokens;", "double mean = total / (double)(tokens > 1 ? tokens - 1 : 1);"),
+ ("alpha k/(grid+1)", "double alpha = (double)k / (double)grid;", "double alpha = (double)k / (double)(grid + 1);"),
+ ("centre drop min", "double centre = sqrt(pmax * pmin);", "double centre = sqrt(pmax);"),
+ ("sym levels", "const float levels = (float)((1 << (bits - 1)) - 1);", "const float levels = (float)((1 << (bits - 1)));"),
+ ("sym round away", "float q = rintf(v[i] / scale);", "float q = roundf(v[i] / scale);"),
+ ("asym zero sign", "float zero = rintf(-lo / scale);", "float zero = rintf(lo / scale);"),
+ ("asym no zero in range", "if (lo > 0.0f) lo = 0.0f;", ";"),
+ ("fq multiply", "wq[o * in + g0 + i] = (double)what[i] / (double)s[g0 + i];", "wq[o * in + g0 + i] = (double)what[i] * (double)s[g0 + i];"),
+ ("err sign", "double e = y - ref[o * tokens + t];", "double e = y + ref[o * tokens + t];"),
+ ("err index", "double e = y - ref[o * tokens + t];", "double e = y - ref[t * out + o];"),
+ ("tie rule", "if (err < best_err) {", "if (err <= best_err) {"),
+ ("pack shift", "rowq[word] |= c << shift;", "rowq[word] |= c << (32 - bits - shift);"),
+ ("mse norm", "err = output_sse(x64, ref, wq, out, in, tokens, row, nthreads) /\n                     ((double)tokens * (double)out);", "err = output_sse(x64, ref, wq, out, in, tokens, row, nthreads) /\n                     ((double)tokens);"),
+ ("v uses w only", "v[i] = W[o * in + g0 + i] * s[g0 + i];\n                    awq_ref_quant_group(v, group, bits, mode, NULL", "v[i] = W[o * in + g0 + i];\n                    awq_ref_quant_group(v, group, bits, mode, NULL"),
+ ("sym clamp hi", "if (q > levels) q = levels;", "if (q > levels - 1.0f) q = levels - 1.0f;"),
+ ("stats chunk reset", "double chunk = 0.0;", "double chunk = total;"),
+ ("dot drops last", "for (int64_t i = 0; i < n; ++i)\n        acc += a[i] * b[i];", "for (int64_t i = 0; i + 1 < n; ++i)\n        acc += a[i] * b[i];"),
+ ("asym dequant", "if (what) what[i] = scale * (q - zero);", "if (what) what[i] = scale * q;"),
+ ("sym scale floor", "if (scale < 1e-8f) scale = 1e-8f;\n        for (int64_t i = 0; i < g; ++i) {\n            float q = rintf(v[i] / scale);\n            if (q < -levels", "for (int64_t i = 0; i < g; ++i) {\n            float q = rintf(v[i] / scale);\n            if (q < -levels"),
+]
+
+
+@pytest.mark.parametrize("name,before,after", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, before, after):
+    src = open(SRC).read()
+    assert before in src, f"pattern for '{name}' no longer in the oracle source"
+    (tmp_path / "awq_oracle.c").write_text(src.replace(before, after, 1))
+    shutil.copy(os.path.join(ROOT, "oracle", "awq_oracle.h"), tmp_path / "awq_oracle.h")
+    lib = tmp_path / "liboracle.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", str(lib), str(tmp_path / "awq_oracle.c"), "-lm"], check=True)
+    env = dict(os.environ, AWQ_ORACLE_LIB=str(lib), OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, cwd=ROOT, timeout=600)
+    assert r.returncode != 0, f"planted mistake '{name}' passed every pin:\n{r.stdout[-500:]}"
