@@ -1,0 +1,207 @@
+"""Benchmark of the AWQ per-layer scale search and pack on one MI355X.
+
+One step = the whole path for one layer with its inputs resident in HBM:
+activation statistics, candidate scales, the fused error search over every
+alpha, the reduction and argmin, and the final quantize-and-pack. The workload
+is the 4096x4096 fp16 linear layer with 256 calibration tokens, int4
+symmetric, group 128, grid 20 (21 alpha candidates), on seeded synthetic data.
+
+Prints one JSON line. Timing: HIP events recorded on the stream the library
+launches on (torch's current stream), around every stage of every step;
+`value` is alpha-candidate MACs per second over whole steps.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+METRIC = "AWQ search: α-candidate·MACs/s + ms per layer (4096×4096, 256 tok, g128, 21 α)"
+SEARCH_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_search.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "k_search_linear4096_pmc.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="linear_4096x4096_t256",
+                   help="workload name (one of synth.CONFIGS)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run a plain device copy of known size (HBM counter calibration)")
+    return p.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(alg_launch):
+    """HBM bytes per search launch from committed rocprofv3 counters, or None
+    when none are committed for the current kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    with open(PMC_FILE) as f:
+        d = json.load(f)
+    if d.get("k_search_source_sha256_16") != source_hash(SEARCH_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(spec, lay, target_s):
+    """The oracle as it stands, on the first R rows of the same layer (all tokens,
+    all columns, every candidate), R grown until the run takes ~target_s."""
+    import numpy as np
+    from oracle import oracle as ref
+    from post_weight_quantization_30_amd import synth
+    Xf = synth.storage_to_f32(lay["X"], spec.dtype)
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    rows = 8
+    while True:
+        Wf = synth.storage_to_f32(lay["W"][:rows], spec.dtype)
+        t0 = time.perf_counter()
+        xmag = ref.act_stats(Xf)
+        _, best, s_best, _ = ref.search(Wf, Xf, xmag, spec.bits, spec.group, spec.grid, spec.mode)
+        ref.quantize_pack(Wf, s_best, spec.bits, spec.group, spec.mode)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or rows >= spec.out:
+            break
+        rows = min(spec.out, int(rows * max(2.0, min(8.0, target_s / max(dt, 1e-3)))))
+    macs = spec.n_alpha * spec.tokens * rows * spec.inn
+    return {"value": macs / dt, "unit": "alpha-candidate MAC/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {spec.out} rows, all {spec.tokens} tokens and {spec.inn} columns, "
+                      f"{spec.n_alpha} candidates; stats + search + pack; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the AWQ search of one layer is measured on a "
+              "single MI355X (sharding over GPUs is described in DESIGN.md, not run).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from post_weight_quantization_30_amd import awq, synth
+
+    spec = synth.BY_NAME[args.config]
+    lay = synth.make_layer(spec)
+    torch.cuda.set_device(0)
+    W = awq.to_device(lay["W"], spec.dtype)
+    X = awq.to_device(lay["X"], spec.dtype)
+    out, n_in, T, grid = spec.out, spec.inn, spec.tokens, spec.grid
+    dev = W.device
+    ws_s = torch.empty(awq.act_stats_workspace_size(T, n_in), dtype=torch.uint8, device=dev)
+    ws = torch.empty(awq.search_workspace_size(out, n_in, T, grid), dtype=torch.uint8, device=dev)
+    xmag = torch.empty(n_in, dtype=torch.float32, device=dev)
+    mse = torch.empty(grid + 1, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    s_best = torch.empty(n_in, dtype=torch.float32, device=dev)
+    qweight = torch.empty((out, awq.words_per_row(n_in, spec.bits)), dtype=torch.int32, device=dev)
+    scales = torch.empty((out, n_in // spec.group), dtype=torch.float32, device=dev)
+    zeros = torch.empty((out, n_in // spec.group), dtype=torch.uint8, device=dev)
+
+    stages = ["stats", "prepare", "search", "finish", "pack"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        awq.act_stats(X, xmag, ws_s)
+        mark(1)
+        awq.search_prepare(xmag, out, T, grid, ws)
+        mark(2)
+        awq.search_candidates(W, X, spec.bits, spec.group, grid, spec.mode, ws)
+        mark(3)
+        awq.search_finish(out, n_in, T, grid, mse, best, s_best, ws)
+        mark(4)
+        awq.quantize_pack(W, s_best, spec.bits, spec.group, spec.mode, qweight, scales, zeros)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {s: [] for s in stages}
+    for ev in events:
+        for i, s in enumerate(stages):
+            per[s].append(ev[i].elapsed_time(ev[i + 1]))
+    gpu_total_ms = events[0][0].elapsed_time(events[-1][5])
+    ms_per_step = gpu_total_ms / args.steps
+    avg = {s: sum(v) / len(v) for s, v in per.items()}
+
+    alpha_macs = spec.alpha_macs
+    value = alpha_macs / (ms_per_step * 1e-3)
+    search_flops = 2.0 * alpha_macs
+    fp32_ops = spec.dtype == "f32" or out < 256 or T < 16
+    peak = PEAK_F32_TFLOPS if fp32_ops else PEAK_F16_TFLOPS
+    achieved = search_flops / (avg["search"] * 1e-3) / 1e12
+    esize = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
+    stats_bytes = T * n_in * esize + 4 * n_in
+    pack_bytes = out * n_in * esize + 4 * n_in + out * n_in * spec.bits / 8 + 5 * out * (n_in // spec.group)
+
+    m = mse.cpu().numpy()
+    b = int(best.item())
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "alpha-candidate MAC/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if spec.dtype == "f16" else spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "out": out, "in": n_in, "tokens": T, "bits": spec.bits,
+                   "group": spec.group, "mode": spec.mode, "n_alpha": spec.n_alpha,
+                   "input_dtype": spec.dtype, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "k_search", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": traffic_from_profile(search_flops)},
+        "stages_ms": avg,
+        "search_alpha_macs_per_s": alpha_macs / (avg["search"] * 1e-3),
+        "stats_gbs": stats_bytes / (avg["stats"] * 1e-3) / 1e9,
+        "pack_gbs": pack_bytes / (avg["pack"] * 1e-3) / 1e9,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "result": {"best_index": b, "best_alpha": b / grid if b >= 0 else None,
+                   "awq_mse": float(m[b]) if b >= 0 else None, "rtn_mse": float(m[0])},
+    }
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calib_bytes"] = src.numel()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(spec, lay, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

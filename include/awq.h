@@ -1,0 +1,154 @@
+/*
+ * awq.h -- C ABI of libawq.so: the AWQ per-layer activation-aware scale
+ * search and final group quantization on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   "AWQ (activation-aware weight quantization)" (pigeon guide), sections
+ *   "How it works" and "The code, line by line": measure each input channel's
+ *   mean activation magnitude s_X; for each alpha on an even grid over [0, 1]
+ *   scale the weight columns by s = s_X^alpha (centred by sqrt(max s * min s)),
+ *   round the scaled weights group-wise, undo the scaling, and measure the mean
+ *   squared layer output error on the calibration inputs; keep the alpha with
+ *   the smallest error. "AWQ vs GPTQ Quantization Architectures Compared",
+ *   "What lands on disk": the deployable result is integer codes plus one scale
+ *   and one zero point per group and output row.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers on the current HIP device unless stated;
+ *     tensors are contiguous and row-major. W is (out, in), X is (tokens, in)
+ *     (y = W x per token). W and X share one element type (awq_dtype).
+ *   - The caller owns every buffer (inputs, outputs and workspace). The library
+ *     keeps no state between calls and allocates no device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *     the call returns before it runs: outputs are valid once the caller has
+ *     synchronised with the stream.
+ *   - Every argument is checked on the host before anything is enqueued. A
+ *     failed check returns a negative status and writes nothing. A failed
+ *     kernel launch returns AWQ_ERR_HIP. No C++ exception crosses the ABI.
+ */
+#ifndef AWQ_H
+#define AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { AWQ_F32 = 0, AWQ_F16 = 1, AWQ_BF16 = 2 } awq_dtype;
+typedef enum { AWQ_SYM = 0, AWQ_ASYM = 1 } awq_qmode;
+
+enum {
+    AWQ_OK = 0,
+    AWQ_ERR_INVALID_ARG = -1, /* null pointer, size < 1, in % group != 0, bits outside [2, 8], grid < 1, bad enum */
+    AWQ_ERR_WORKSPACE = -2,   /* ws_bytes below the matching *_workspace_size() (or ws == NULL with a nonzero size) */
+    AWQ_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+    AWQ_ERR_NONFINITE = -4,   /* reserved: a search whose candidate errors are all non-finite reports best = -1 on the device */
+    AWQ_ERR_UNSUPPORTED = -5  /* valid arguments outside what the GPU kernels implement (see each call) */
+};
+
+/* Largest grid accepted by awq_search / awq_s_table (grid + 1 candidates). */
+#define AWQ_MAX_GRID 1024
+
+/* Step 1, activation statistics ("AWQ (activation-aware weight quantization)",
+ * "How it works" step 1 and the first line explained in "The code, line by line"):
+ *   xmag[j] = fp32( mean_t |X[t, j]| + 1e-8 )
+ * summed in fp64 in a fixed order: sequentially within consecutive 64-token
+ * chunks, then the chunk sums in ascending chunk order; bitwise reproducible.
+ *   X:    device, (tokens, in) of `dtype`.
+ *   xmag: device, fp32[in] (output).
+ *   ws:   device scratch of at least awq_act_stats_workspace_size(tokens, in) bytes.
+ */
+int awq_act_stats(const void *X, int dtype, int64_t tokens, int64_t in, float *xmag,
+                  void *ws, size_t ws_bytes, void *stream);
+size_t awq_act_stats_workspace_size(int64_t tokens, int64_t in);
+
+/* Step 2 alone, the candidate scales ("The code, line by line": grid + 1 evenly
+ * spaced alpha in [0, 1] including 0; s = xmag^alpha divided by
+ * sqrt(max s * min s)). alpha_k = k / grid in fp64, the power and centring in
+ * fp64, one rounding to fp32:
+ *   s_table[k][j] = fp32( xmag[j]^alpha_k / sqrt(max_j xmag^alpha_k * min_j xmag^alpha_k) )
+ *   xmag:    device fp32[in];  s_table: device fp32[(grid + 1) * in] (output).
+ * awq_search computes the same table internally; this call exposes it. */
+int awq_s_table(const float *xmag, int64_t in, int grid, float *s_table, void *stream);
+
+/* Steps 2-4, the search ("Source code", awq() listing of the pigeon guide;
+ * "AWQ: move the error away from what matters", awq_scales()). For every
+ * candidate k = 0..grid, with s = s_table[k]:
+ *   Wq  = Q(W diag(s)) diag(s)^-1        (group round-to-nearest, see quantize_pack)
+ *   mse[k] = mean over tokens*out of (X Wq^T - X W^T)^2
+ * and best = the smallest k whose mse is strictly below every earlier one
+ * (so the lowest alpha wins ties and a NaN error is never chosen).
+ *   W, X:    device, (out, in) and (tokens, in) of `dtype`.
+ *   xmag:    device fp32[in], as written by awq_act_stats (any positive values work).
+ *   bits:    2..8;  group: divides in;  grid: 1..AWQ_MAX_GRID;  mode: awq_qmode.
+ *   mse:     device fp64[grid + 1] (output).
+ *   best:    device int32[1] (output); -1 when no candidate error is finite.
+ *   s_best:  device fp32[in] (output): s_table[best], or all ones when best = -1.
+ *            Deploy by multiplying W's columns by it and dividing the layer's
+ *            input by it upstream.
+ *   ws:      device scratch of at least awq_search_workspace_size(...) bytes.
+ * The GPU kernels evaluate the error as X (Wq - W)^T (equal to the difference
+ * of the two products by linearity), accumulating in fp32 and summing squares
+ * in fp64; mse is accurate to about 1e-5 relative, not bitwise. Operands are
+ * 16-bit (the input type) for fp16/bf16 layers with at least 256 rows and 16
+ * tokens, and exact fp32 otherwise (fp32 inputs, or layers too small for the
+ * unbiased 16-bit rounding of Wq - W to average out below 1e-3).
+ * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128}. */
+int awq_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+               int64_t tokens, const float *xmag, int bits, int group, int grid, int mode,
+               double *mse, int32_t *best, float *s_best, void *ws, size_t ws_bytes,
+               void *stream);
+size_t awq_search_workspace_size(int64_t out, int64_t in, int64_t tokens, int grid);
+
+/* awq_search in its three stages, in this order on one stream with one
+ * workspace (awq_search is exactly the three calls). They let a caller time or
+ * profile the error kernel alone, and they are where a search sharded over
+ * devices would combine its partial sums. Arguments mean what they mean for
+ * awq_search; each stage validates its own arguments the same way.
+ *   awq_search_prepare:    the s-table and its reciprocals into ws (step 2).
+ *   awq_search_candidates: the fused quantize-dequantize-error kernel; leaves
+ *                          one fp64 partial sum of squares per (candidate,
+ *                          block of 16 rows x 256 tokens) in ws. Needs the
+ *                          prepared ws.
+ *   awq_search_finish:     fixed-order reduction of the partials into mse,
+ *                          argmin into best, s_best. Needs the candidates' ws. */
+int awq_search_prepare(const float *xmag, int64_t out, int64_t in, int64_t tokens, int grid,
+                       void *ws, size_t ws_bytes, void *stream);
+int awq_search_candidates(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                          int64_t tokens, int bits, int group, int grid, int mode, void *ws,
+                          size_t ws_bytes, void *stream);
+int awq_search_finish(int64_t out, int64_t in, int64_t tokens, int grid, double *mse,
+                      int32_t *best, float *s_best, void *ws, size_t ws_bytes, void *stream);
+
+/* Step 5, final quantization and packing of W diag(s). Per output row o and
+ * group of `group` consecutive columns, with v = fp32(W[o, j] * s[j]):
+ *   symmetric ("GPTQ and AWQ weight quantisation", "Per-group symmetric int4
+ *   (RTN)" and the n-bit form in "Output MSE vs bit width"): L = 2^(bits-1) - 1,
+ *     scale = max(max|v| / L, 1e-8), q = clamp(rne(v / scale), -L-1, L),
+ *     code = q + 2^(bits-1), zero = 2^(bits-1);
+ *   asymmetric ("AWQ vs GPTQ Quantization Architectures Compared", group_params
+ *   and rtn in "GPTQ: compensate the error you just made"): maxq = 2^bits - 1,
+ *     lo = min(min v, 0), hi = max(max v, 0), scale = max((hi - lo) / maxq, 1e-8),
+ *     zero = rne(-lo / scale), code = clamp(rne(v / scale) + zero, 0, maxq).
+ * All in fp32 with IEEE division and round-half-to-even, in exactly this order:
+ * the outputs are bit-exact. Dequantize as scale * (code - zero).
+ *   W:       device (out, in) of `dtype`;  s: device fp32[in] (e.g. s_best).
+ *   qweight: device uint32[out][in * bits / 32 rounded up] (output): code i of a
+ *            row at bits [i*bits, (i+1)*bits) of the row's little-endian stream
+ *            of 32-bit words; every row starts on a word boundary.
+ *   scales:  device fp32[out][in / group] (output).
+ *   zeros:   device uint8[out][in / group] (output).
+ * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128, 256, 512, 1024, 2048}. */
+int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s,
+                      int bits, int group, int mode, uint32_t *qweight, float *scales,
+                      uint8_t *zeros, void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *awq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,209 @@
+// abi.hip -- the extern "C" entry points of libawq.so (declared in include/awq.h).
+//
+// Every entry point validates all arguments on the host before it enqueues
+// anything; on a failed check it returns a negative status and writes nothing.
+// The library allocates no device memory: scratch comes from the caller's
+// workspace.
+#include "awq_internal.h"
+
+namespace {
+
+bool valid_dtype(int d) { return d == AWQ_F32 || d == AWQ_F16 || d == AWQ_BF16; }
+bool valid_mode(int m) { return m == AWQ_SYM || m == AWQ_ASYM; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+
+bool search_group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+bool pack_group_ok(int g)
+{
+    return g == 32 || g == 64 || g == 128 || g == 256 || g == 512 || g == 1024 || g == 2048;
+}
+
+size_t stats_ws_bytes(int64_t tokens, int64_t in)
+{
+    const int64_t nchunk = (tokens + 63) / 64;
+    return (size_t)(nchunk * in) * sizeof(double);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *awq_status_string(int status)
+{
+    switch (status) {
+    case AWQ_OK: return "ok";
+    case AWQ_ERR_INVALID_ARG: return "invalid argument";
+    case AWQ_ERR_WORKSPACE: return "workspace too small";
+    case AWQ_ERR_HIP: return "HIP runtime error";
+    case AWQ_ERR_NONFINITE: return "no finite candidate error";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported by the GPU kernels";
+    default: return "unknown status";
+    }
+}
+
+size_t awq_act_stats_workspace_size(int64_t tokens, int64_t in)
+{
+    if (tokens < 1 || in < 1)
+        return 0;
+    return stats_ws_bytes(tokens, in);
+}
+
+int awq_act_stats(const void *X, int dtype, int64_t tokens, int64_t in, float *xmag, void *ws,
+                  size_t ws_bytes, void *stream)
+{
+    if (!X || !xmag || tokens < 1 || in < 1 || !valid_dtype(dtype))
+        return AWQ_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < stats_ws_bytes(tokens, in))
+        return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_act_stats(X, dtype, tokens, in, xmag, (double *)ws,
+                                            (hipStream_t)stream));
+}
+
+int awq_s_table(const float *xmag, int64_t in, int grid, float *s_table, void *stream)
+{
+    if (!xmag || !s_table || in < 1 || grid < 1 || grid > AWQ_MAX_GRID)
+        return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_s_table(xmag, in, grid, s_table, nullptr, nullptr,
+                                          (hipStream_t)stream));
+}
+
+size_t awq_search_workspace_size(int64_t out, int64_t in, int64_t tokens, int grid)
+{
+    if (out < 1 || in < 1 || tokens < 1 || grid < 1 || grid > AWQ_MAX_GRID)
+        return 0;
+    return awq::search_ws_layout(out, in, tokens, grid).total;
+}
+
+namespace {
+
+int check_search_shape(int64_t out, int64_t in, int64_t tokens, int grid)
+{
+    if (out < 1 || in < 1 || tokens < 1 || grid < 1 || grid > AWQ_MAX_GRID)
+        return AWQ_ERR_INVALID_ARG;
+    return AWQ_OK;
+}
+
+int check_workspace(int64_t out, int64_t in, int64_t tokens, int grid, const void *ws,
+                    size_t ws_bytes, awq::SearchWs *lay)
+{
+    *lay = awq::search_ws_layout(out, in, tokens, grid);
+    if (!ws || ws_bytes < lay->total)
+        return AWQ_ERR_WORKSPACE;
+    if (lay->nblk > (int64_t)0x7fffffff || (tokens + awq::kTokPerBlock - 1) / awq::kTokPerBlock > 65535)
+        return AWQ_ERR_UNSUPPORTED;
+    return AWQ_OK;
+}
+
+int check_candidates(const void *W, const void *X, int dtype, int64_t in, int bits, int group,
+                     int mode)
+{
+    if (!W || !X || group < 1 || in % group != 0 || bits < 2 || bits > 8 || !valid_dtype(dtype) ||
+        !valid_mode(mode))
+        return AWQ_ERR_INVALID_ARG;
+    return AWQ_OK;
+}
+
+}  // namespace
+
+int awq_search_prepare(const float *xmag, int64_t out, int64_t in, int64_t tokens, int grid,
+                       void *ws, size_t ws_bytes, void *stream)
+{
+    if (!xmag)
+        return AWQ_ERR_INVALID_ARG;
+    int st = check_search_shape(out, in, tokens, grid);
+    awq::SearchWs lay;
+    if (st == AWQ_OK)
+        st = check_workspace(out, in, tokens, grid, ws, ws_bytes, &lay);
+    if (st != AWQ_OK)
+        return st;
+    char *base = (char *)ws;
+    return hip_status(awq::launch_s_table(xmag, in, grid, (float *)(base + lay.s_off),
+                                          (float *)(base + lay.inv_off),
+                                          (int32_t *)(base + lay.unit_off), (hipStream_t)stream));
+}
+
+int awq_search_candidates(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                          int64_t tokens, int bits, int group, int grid, int mode, void *ws,
+                          size_t ws_bytes, void *stream)
+{
+    int st = check_candidates(W, X, dtype, in, bits, group, mode);
+    if (st == AWQ_OK)
+        st = check_search_shape(out, in, tokens, grid);
+    awq::SearchWs lay;
+    if (st == AWQ_OK)
+        st = check_workspace(out, in, tokens, grid, ws, ws_bytes, &lay);
+    if (st == AWQ_OK && !search_group_ok(group))
+        st = AWQ_ERR_UNSUPPORTED;
+    if (st != AWQ_OK)
+        return st;
+    char *base = (char *)ws;
+    return hip_status(awq::launch_search(W, X, dtype, out, in, tokens, (const float *)(base + lay.s_off),
+                                         (const float *)(base + lay.inv_off),
+                                         (const int32_t *)(base + lay.unit_off), grid + 1, bits,
+                                         group, mode, (double *)(base + lay.part_off),
+                                         (hipStream_t)stream));
+}
+
+int awq_search_finish(int64_t out, int64_t in, int64_t tokens, int grid, double *mse,
+                      int32_t *best, float *s_best, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!mse || !best || !s_best)
+        return AWQ_ERR_INVALID_ARG;
+    int st = check_search_shape(out, in, tokens, grid);
+    awq::SearchWs lay;
+    if (st == AWQ_OK)
+        st = check_workspace(out, in, tokens, grid, ws, ws_bytes, &lay);
+    if (st != AWQ_OK)
+        return st;
+    char *base = (char *)ws;
+    return hip_status(awq::launch_reduce_argmin((const double *)(base + lay.part_off), lay.nblk,
+                                                grid + 1, out, tokens, in,
+                                                (const float *)(base + lay.s_off), mse, best,
+                                                s_best, (hipStream_t)stream));
+}
+
+int awq_search(const void *W, const void *X, int dtype, int64_t out, int64_t in, int64_t tokens,
+               const float *xmag, int bits, int group, int grid, int mode, double *mse,
+               int32_t *best, float *s_best, void *ws, size_t ws_bytes, void *stream)
+{
+    // Validate everything for all three stages before the first launch.
+    if (!xmag || !mse || !best || !s_best)
+        return AWQ_ERR_INVALID_ARG;
+    int st = check_candidates(W, X, dtype, in, bits, group, mode);
+    if (st == AWQ_OK)
+        st = check_search_shape(out, in, tokens, grid);
+    awq::SearchWs lay;
+    if (st == AWQ_OK)
+        st = check_workspace(out, in, tokens, grid, ws, ws_bytes, &lay);
+    if (st == AWQ_OK && !search_group_ok(group))
+        st = AWQ_ERR_UNSUPPORTED;
+    if (st != AWQ_OK)
+        return st;
+    st = awq_search_prepare(xmag, out, in, tokens, grid, ws, ws_bytes, stream);
+    if (st == AWQ_OK)
+        st = awq_search_candidates(W, X, dtype, out, in, tokens, bits, group, grid, mode, ws,
+                                   ws_bytes, stream);
+    if (st == AWQ_OK)
+        st = awq_search_finish(out, in, tokens, grid, mse, best, s_best, ws, ws_bytes, stream);
+    return st;
+}
+
+int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s, int bits,
+                      int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros,
+                      void *stream)
+{
+    if (!W || !s || !qweight || !scales || !zeros)
+        return AWQ_ERR_INVALID_ARG;
+    if (out < 1 || in < 1 || group < 1 || in % group != 0 || bits < 2 || bits > 8 ||
+        !valid_dtype(dtype) || !valid_mode(mode))
+        return AWQ_ERR_INVALID_ARG;
+    if (!pack_group_ok(group))
+        return AWQ_ERR_UNSUPPORTED;
+    if ((out * (in / 32) + 255) / 256 > (int64_t)0x7fffffff)
+        return AWQ_ERR_UNSUPPORTED;
+    return hip_status(awq::launch_pack(W, dtype, out, in, s, bits, group, mode, qweight, scales,
+                                       zeros, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+// k_pack.hip -- final group quantization of W diag(s) and bit packing (step 5).
+//
+// Quantizer, fp32 in this exact operation order (bit-exact contract):
+//   v = w * s
+//   symmetric ("GPTQ and AWQ weight quantisation", "Per-group symmetric int4
+//   (RTN)" and the n-bit form under "Output MSE vs bit width"):
+//     scale = max(max|v| / L, 1e-8), q = clamp(rne(v / scale), -L-1, L), code = q + 2^(b-1)
+//   asymmetric ("AWQ vs GPTQ Quantization Architectures Compared", group_params
+//   and rtn under "GPTQ: compensate the error you just made"):
+//     lo = min(min v, 0), hi = max(max v, 0), scale = max((hi - lo) / maxq, 1e-8),
+//     zero = rne(-lo / scale), code = clamp(rne(v / scale) + zero, 0, maxq)
+// Divisions are IEEE (hipcc's default correctly rounded fp32 division), the
+// library is built with -ffp-contract=off and rintf is v_rndne_f32.
+//
+// Layout: one lane owns 32 consecutive columns of one row. 32 codes of b bits
+// fill exactly b 32-bit words, so a lane writes whole words of the row's
+// little-endian bit stream with no neighbour; a group of G columns spans G/32
+// adjacent lanes, whose max/min are combined with xor shuffles. Loads and
+// stores of a wave are contiguous. HBM bound: read W (2 or 4 B per weight),
+// write b/8 B per weight plus 5 B per group.
+#include "awq_internal.h"
+
+#include <math.h>
+
+namespace awq {
+
+template <int BITS>
+__device__ __forceinline__ void pack_store(const uint32_t (&code)[32], uint32_t *dst)
+{
+    uint32_t word[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k)
+        word[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int bit = i * BITS;
+        const int wi = bit >> 5, sh = bit & 31;
+        word[wi] |= code[i] << sh;
+        if (sh + BITS > 32)
+            word[wi + 1] |= code[i] >> (32 - sh);
+    }
+#pragma unroll
+    for (int k = 0; k < BITS; ++k)
+        dst[k] = word[k];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, int64_t out,
+                                                        int64_t in, const float *__restrict__ s,
+                                                        int bits, int lanes_per_group, int mode,
+                                                        uint32_t *__restrict__ qweight,
+                                                        float *__restrict__ scales,
+                                                        uint8_t *__restrict__ zeros)
+{
+    const int64_t chunks = in / 32;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool active = gid < out * chunks;
+    const int64_t row = active ? gid / chunks : 0;
+    const int64_t ch = active ? gid % chunks : 0;
+
+    float v[32];
+    if (active) {
+        const T *wp = W + row * in + ch * 32;
+        const float *sp = s + ch * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float w8[8];
+            widen8<T>(load8(wp + q * 8), w8);
+            const f32x8 s8 = *reinterpret_cast<const f32x8 *>(sp + q * 8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[q * 8 + i] = w8[i] * s8[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            v[i] = 0.f;
+    }
+
+    uint32_t code[32];
+    float scale, zero;
+    if (mode == AWQ_SYM) {
+        const float levels = (float)((1 << (bits - 1)) - 1);
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            m = fmaxf(m, fabsf(v[i]));
+        for (int off = 1; off < lanes_per_group; off <<= 1)
+            m = fmaxf(m, __shfl_xor(m, off));
+        scale = fmaxf(m / levels, 1e-8f);
+        zero = (float)(1 << (bits - 1));
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            float q = rintf(v[i] / scale);
+            q = fminf(fmaxf(q, -levels - 1.0f), levels);
+            code[i] = (uint32_t)((int)q + (1 << (bits - 1)));
+        }
+    } else {
+        const float maxq = (float)((1 << bits) - 1);
+        float lo = 0.f, hi = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            lo = fminf(lo, v[i]);
+            hi = fmaxf(hi, v[i]);
+        }
+        for (int off = 1; off < lanes_per_group; off <<= 1) {
+            lo = fminf(lo, __shfl_xor(lo, off));
+            hi = fmaxf(hi, __shfl_xor(hi, off));
+        }
+        scale = fmaxf((hi - lo) / maxq, 1e-8f);
+        zero = rintf(-lo / scale);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            float q = rintf(v[i] / scale) + zero;
+            q = fminf(fmaxf(q, 0.0f), maxq);
+            code[i] = (uint32_t)(int)q;
+        }
+    }
+    if (!active)
+        return;
+
+    uint32_t *dst = qweight + row * (chunks * bits) + ch * bits;
+    switch (bits) {
+    case 2: pack_store<2>(code, dst); break;
+    case 3: pack_store<3>(code, dst); break;
+    case 4: pack_store<4>(code, dst); break;
+    case 5: pack_store<5>(code, dst); break;
+    case 6: pack_store<6>(code, dst); break;
+    case 7: pack_store<7>(code, dst); break;
+    default: pack_store<8>(code, dst); break;
+    }
+    if (ch % lanes_per_group == 0) {
+        const int64_t gi = row * (in / (32 * lanes_per_group)) + ch / lanes_per_group;
+        scales[gi] = scale;
+        zeros[gi] = (uint8_t)(int)zero;
+    }
+}
+
+hipError_t launch_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s, int bits,
+                       int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros,
+                       hipStream_t st)
+{
+    const int lpg = group / 32;
+    const int64_t threads = out * (in / 32);
+    dim3 grid((unsigned)((threads + 255) / 256));
+    switch (dtype) {
+    case AWQ_F32:
+        hipLaunchKernelGGL(k_quantize_pack<float>, grid, dim3(256), 0, st, (const float *)W, out, in,
+                           s, bits, lpg, mode, qweight, scales, zeros);
+        break;
+    case AWQ_F16:
+        hipLaunchKernelGGL(k_quantize_pack<f16>, grid, dim3(256), 0, st, (const f16 *)W, out, in, s,
+                           bits, lpg, mode, qweight, scales, zeros);
+        break;
+    default:
+        hipLaunchKernelGGL(k_quantize_pack<bf16>, grid, dim3(256), 0, st, (const bf16 *)W, out, in,
+                           s, bits, lpg, mode, qweight, scales, zeros);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace awq
