@@ -51,7 +51,7 @@ struct SearchWs {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kRowsPerBlock = 16;    // output rows per search block (one MFMA N tile)
-constexpr int kTokPerBlock = 256;    // calibration tokens per search block (4 waves x 64)
+constexpr int kTokPerBlock = 256;    // calibration tokens per search block (8 waves x 32)
 // Below these sizes the search runs with fp32 MFMA operands (see k_search.hip).
 constexpr int64_t kMinRows16 = 256;
 constexpr int64_t kMinTokens16 = 16;

@@ -38,13 +38,15 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace awq {
 
-constexpr int kWaves = 4;
-constexpr int kTokPerWave = 64;
+constexpr int kWaves = 8;               // two per SIMD
+constexpr int kTokPerWave = kTokPerBlock / kWaves;
 constexpr int kTT = kTokPerWave / 16;   // 16-token MFMA tiles per wave
-constexpr int kMaxNA = 21;              // accumulator budget: 16 * NA registers per lane
-constexpr int kLdsBudget = 86016;       // bytes of LDS for the D tiles of one group
+constexpr int kMaxNA = 11;              // candidates per block: 16 * NA accumulator registers per lane
+constexpr int kLdsBudget = 160 * 1024 - 512;   // bytes of LDS per block
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16> {
@@ -70,6 +72,29 @@ template <> struct Mfma<float> {
         return c;
     }
 };
+
+// Max / min over the four lanes l, l^16, l^32, l^48 (the four 8-column
+// slices of one row in the B-operand layout) with two lane-swap steps:
+// permlane16_swap(x, x) hands lane l the values of lanes l and l^16, and
+// permlane32_swap(x, x) those of l and l^32.
+__device__ __forceinline__ float lanes4_max(float m)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(m), __float_as_int(m), false, false);
+    m = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
+    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+__device__ __forceinline__ float lanes4_min(float m)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(m), __float_as_int(m), false, false);
+    m = fminf(__int_as_float(a[0]), __int_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
+    return fminf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+
+// MFMA instructions per 32-column step of one 16x16 tile.
+template <typename T> struct MfmaCount { static constexpr int value = 1; };
+template <> struct MfmaCount<float> { static constexpr int value = 8; };
 
 template <typename T> __device__ __forceinline__ typename Vec8<T>::type narrow8(const float *d);
 template <> __device__ __forceinline__ f32x8 narrow8<float>(const float *d)
@@ -103,46 +128,20 @@ template <> __device__ __forceinline__ f16x8 narrow8<f16>(const float *d)
     return r;
 }
 
-// D for one candidate tile: q = rne(v / scale) (clamped to the asymmetric
-// code range; the symmetric clamp of the exact quantizer can never bind,
-// since |v| <= max|v| = L * scale), d = (q * scale - v) / s, rounded to the
-// operand type and stored as this lane's 8-column slices of the B operand.
-// The quotient is v * (1/scale); EXACT adds one residual step that makes it
-// the correctly rounded quotient (Markstein: with y = RN(1/b) and
-// q0 = RN(a*y), RN(q0 + RN(a - b*q0)*y) = RN(a/b)). EXACT is used when s is
-// all ones (alpha = 0 or flat activations): v then holds the stored 16-bit
-// weights, which land exactly on rounding ties often enough that the
-// one-ulp difference of the plain product would flip codes the exact
-// quantizer keeps. For other candidates v = w * s is unstructured and such
-// flips have probability ~1e-7 per weight.
-template <typename TOp, int KS, bool ASYM, bool EXACT>
-__device__ __forceinline__ void emit_tile(const float (&v)[KS][8], float scale, float rs, float zlo,
-                                          float zhi, const float *__restrict__ irow,
-                                          typename Vec8<TOp>::type *dst)
-{
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const f32x8 i8 = *reinterpret_cast<const f32x8 *>(irow + ks * 32);
-        float d[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float u = v[ks][i] * rs;
-            if (EXACT)
-                u = fmaf(fmaf(-u, scale, v[ks][i]), rs, u);
-            float q = rintf(u);
-            if (ASYM)
-                q = fminf(fmaxf(q, zlo), zhi);
-            d[i] = fmaf(q, scale, -v[ks][i]) * i8[i];
-        }
-        dst[ks * 64] = narrow8<TOp>(d);
-    }
-}
-
 template <typename TOp, int G>
 struct SearchShape {
-    static constexpr int KS = G / 32;                                  // 32-column MFMA steps per group
+    static constexpr int KS = G / 32;   // 32-column MFMA steps per group
     static constexpr int kTileBytes = KS * 64 * (int)sizeof(typename Vec8<TOp>::type);
-    static constexpr int NA = kLdsBudget / kTileBytes < kMaxNA ? kLdsBudget / kTileBytes : kMaxNA;
+    // LDS per block for NA candidates: two buffers (this group's D tiles, the
+    // next group's) of NA + 1 tiles (the extra one takes the writes of idle
+    // generation slots), s and 1/s rows for two groups, the epilogue sums.
+    static constexpr int lds_bytes(int na)
+    {
+        return 2 * (na + 1) * kTileBytes + 2 * 2 * na * G * 4 + kWaves * na * 8;
+    }
+    static constexpr int fit(int na) { return na > 1 && lds_bytes(na) > kLdsBudget ? fit(na - 1) : na; }
+    static constexpr int NA = fit(kMaxNA);
+    static constexpr int GPW = (NA + kWaves - 1) / kWaves;   // tiles each wave builds per group
 };
 
 // Stored inputs -> MFMA operand type (identity, or exact widening to fp32).
@@ -163,19 +162,118 @@ template <typename TIn> struct ToOp<TIn, float> {
     }
 };
 
-// TIn: stored element type of W and X. TOp: MFMA operand type (TIn for the
-// 16-bit path, float for the fp32-operand path).
-template <typename TIn, typename TOp, int G>
-__global__ __launch_bounds__(256, 1) void k_search(
+// D for one candidate tile: q = rne(v / scale) (clamped to the asymmetric
+// code range; the symmetric clamp of the exact quantizer can never bind,
+// since |v| <= max|v| = L * scale), d = (q * scale - v) / s, rounded to the
+// operand type and stored as this lane's 8-column slices of the B operand.
+//
+// The plain path takes the quotient as v * rcp(scale) and scale as
+// max|v| * (1/L): the error sum tolerates those last-bit differences. EXACT
+// reproduces the exact quantizer's arithmetic: IEEE scale and zero, and the
+// correctly rounded quotient from one residual step (Markstein: with
+// y = RN(1/b) and q0 = RN(a*y), RN(q0 + RN(a - b*q0)*y) = RN(a/b)). It is
+// used for the candidate whose scales are all ones (alpha = 0): v then holds
+// the stored 16-bit weights, which sit exactly on rounding ties often enough
+// that a one-ulp quotient difference would flip codes the exact quantizer
+// keeps (a systematic 2e-4 shift of the RTN error). For other candidates
+// v = w * s is unstructured and such flips have probability ~1e-7 per weight.
+template <typename TOp, int KS, bool ASYM, bool EXACT>
+__device__ __forceinline__ void build_tile(const float (&v)[KS][8], float levels, float maxq,
+                                           float inv_levels, float inv_maxq,
+                                           const float *__restrict__ irow,
+                                           typename Vec8<TOp>::type *dst)
+{
+    float scale, rs, zlo = 0.f, zhi = 0.f;
+    if (!ASYM) {
+        float m = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                m = fmaxf(m, fabsf(v[ks][i]));
+        m = lanes4_max(m);
+        if (EXACT) {
+            scale = fmaxf(m / levels, 1e-8f);
+            rs = 1.0f / scale;
+        } else {
+            scale = fmaxf(m * inv_levels, 1e-8f);
+            rs = __builtin_amdgcn_rcpf(scale);
+        }
+    } else {
+        float lo = 0.f, hi = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                lo = fminf(lo, v[ks][i]);
+                hi = fmaxf(hi, v[ks][i]);
+            }
+        lo = lanes4_min(lo);
+        hi = lanes4_max(hi);
+        float zero;
+        if (EXACT) {
+            scale = fmaxf((hi - lo) / maxq, 1e-8f);
+            rs = 1.0f / scale;
+            zero = rintf(-lo / scale);
+        } else {
+            scale = fmaxf((hi - lo) * inv_maxq, 1e-8f);
+            rs = __builtin_amdgcn_rcpf(scale);
+            zero = rintf(-lo * rs);
+        }
+        zlo = -zero;
+        zhi = maxq - zero;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const f32x8 i8 = *reinterpret_cast<const f32x8 *>(irow + ks * 32);
+        float d[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float u = v[ks][i] * rs;
+            if (EXACT)
+                u = fmaf(fmaf(-u, scale, v[ks][i]), rs, u);
+            float q = rintf(u);
+            if (ASYM)
+                q = fminf(fmaxf(q, zlo), zhi);
+            d[i] = fmaf(q, scale, -v[ks][i]) * i8[i];
+        }
+        dst[ks * 64] = narrow8<TOp>(d);
+    }
+}
+
+// One block: 16 output rows x 256 tokens x NA candidates (candidates a0 ..
+// a0 + NA - 1, a0 = NA * blockIdx.z), 4 waves, one wave per SIMD (the 16 * NA
+// accumulator registers per lane leave room for nothing else on the SIMD).
+//
+// Software pipeline over groups of G input columns, one barrier per group:
+// the D tiles live in two LDS buffers selected by group parity. In the
+// iteration of group g every wave
+//   1. issues the loads of group g+1's X fragments and weights (registers),
+//   2. waits at the barrier (group g's tiles are complete; group g-1's have
+//      been read by everyone),
+//   3. runs the MFMAs of all NA candidates of group g (B fragments read one
+//      candidate ahead),
+//   4. builds its share of group g+1's tiles (wave w: candidates w, w+4, ...)
+//      into the other buffer.
+// On gfx950 a wave's MFMA and VALU time add up rather than overlap, so the
+// pipeline's job is to keep LDS and global-memory latency off the critical
+// path, not to hide the VALU work.
+template <typename TIn, typename TOp, int G, bool ASYM>
+__global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     const TIn *__restrict__ W, const TIn *__restrict__ X, int64_t out, int64_t in, int64_t tokens,
     const float *__restrict__ s_tab, const float *__restrict__ inv_tab,
-    const int32_t *__restrict__ unit, int n_alpha, int bits, int mode, double *__restrict__ partial)
+    const int32_t *__restrict__ unit, int n_alpha, int bits, double *__restrict__ partial)
 {
     typedef typename Vec8<TOp>::type V8;
+    typedef typename Vec8<TIn>::type V8in;
     constexpr int KS = SearchShape<TOp, G>::KS;
     constexpr int NA = SearchShape<TOp, G>::NA;
+    constexpr int GPW = SearchShape<TOp, G>::GPW;
 
-    __shared__ V8 dtile[NA][KS][64];
+    __shared__ V8 dbuf[2][NA + 1][KS][64];
+    // s and 1/s of this block's candidates over one group of columns, for
+    // the group being built; double-buffered by group parity.
+    __shared__ f32x4 stab[2][2][NA][G / 4];
     __shared__ double wsum[kWaves][NA];
 
     const int lane = threadIdx.x & 63;
@@ -193,6 +291,129 @@ __global__ __launch_bounds__(256, 1) void k_search(
 
     const float levels = (float)((1 << (bits - 1)) - 1);
     const float maxq = (float)((1 << bits) - 1);
+    const float inv_levels = 1.0f / levels;
+    const float inv_maxq = 1.0f / maxq;
+
+    // X rows of this wave's tokens, clamped to the last token (always in
+    // bounds); tokens past the end are zeroed after the load.
+    const TIn *xrow[kTT];
+    bool tok_ok[kTT];
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+        const int64_t t = tok0 + tt * 16 + r;
+        tok_ok[tt] = t < tokens;
+        xrow[tt] = X + (tok_ok[tt] ? t : tokens - 1) * in + c * 8;
+    }
+    const TIn *wrow = W + row_c * in + c * 8;
+
+    // Generation slots of this wave: slots wave + 8 i, of which the first
+    // na are real. Waves 0-2 get two slots when na > 8, so SIMDs 0-2 build
+    // three tiles per group and SIMD 3 (waves 3 and 7) two; slot s builds
+    // candidate (s - 3) mod na, which puts candidate 0 -- the one built with
+    // the slower exact path in the first pass -- on wave 3, i.e. on SIMD 3.
+    // Idle slots build a valid candidate's tile into the spare slot NA.
+    int gen_a[GPW], gen_slot[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int a = wave + kWaves * i;
+        const bool real = a < na;
+        const int cand = (a + 3 * (na - 1)) % na;   // (a - 3) mod na, a < 8 + na
+        gen_a[i] = a0 + (real ? cand : na - 1);
+        gen_slot[i] = real ? cand : NA;
+    }
+    // Slots after the first are built only when they hold a candidate (the
+    // first slot of every wave is always real or the spare).
+    const int gen_n = wave + kWaves < na ? (wave + 2 * kWaves < na ? 3 : 2) : 1;
+    // Which tiles take the exact quotient path: the candidate whose scales
+    // are all ones (alpha = 0: slot 0 of wave 0 in the first pass), or every
+    // candidate when all of them are all ones (flat activations, where the
+    // candidates must come out identical). Decided once per wave, outside the
+    // group loop, so each loop body is free of per-tile branches.
+    const bool all_unit = unit[n_alpha - 1] != 0;
+    const int exm = all_unit ? 2 : (a0 == 0 && gen_slot[0] == 0 ? 1 : 0);
+    // Waves whose 64 tokens are all in range never touch their X fragments
+    // between load and MFMA, so the loads' latency stays hidden.
+    const bool tok_full = tok0 + kTokPerWave <= tokens;
+
+    V8 xa[kTT][KS];
+    auto load_x = [&](int64_t k0, V8 (&xd)[kTT][KS]) {
+#pragma unroll
+        for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                xd[tt][ks] = ToOp<TIn, TOp>::run(load8(xrow[tt] + k0 + ks * 32));
+        if (!tok_full) {
+            const V8 zero8 = {};
+#pragma unroll
+            for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    xd[tt][ks] = tok_ok[tt] ? xd[tt][ks] : zero8;
+        }
+    };
+    auto load_w = [&](int64_t k0, V8in (&wd)[KS]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            wd[ks] = load8(wrow + k0 + ks * 32);
+    };
+    // s and 1/s rows of group `gi`: fetched into registers (3 float4 per
+    // thread at NA = 11, G = 128), stored to LDS later so the fetch latency
+    // hides behind a whole iteration.
+    constexpr int kSEntries = 2 * NA * (G / 4);
+    constexpr int kSPer = (kSEntries + kWaves * 64 - 1) / (kWaves * 64);
+    auto fetch_s = [&](int64_t gi, f32x4 (&sv)[kSPer]) {
+#pragma unroll
+        for (int i = 0; i < kSPer; ++i) {
+            const int e = (int)threadIdx.x + kWaves * 64 * i;
+            const int ec = e < kSEntries ? e : kSEntries - 1;
+            const int which = ec / (NA * (G / 4));          // 0: s, 1: 1/s
+            const int a = (ec / (G / 4)) % NA;
+            const int q = ec % (G / 4);
+            const int ag = a0 + (a < na ? a : na - 1);
+            const float *base = which ? inv_tab : s_tab;
+            sv[i] = *reinterpret_cast<const f32x4 *>(base + (int64_t)ag * in + gi * G + q * 4);
+        }
+    };
+    auto store_s = [&](int sp, const f32x4 (&sv)[kSPer]) {
+#pragma unroll
+        for (int i = 0; i < kSPer; ++i) {
+            const int e = (int)threadIdx.x + kWaves * 64 * i;
+            if (e < kSEntries)
+                (&stab[sp][0][0][0])[e] = sv[i];
+        }
+    };
+    auto build_slot = [&](auto exact_tag, const float (&wg)[KS][8], int par, int i) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+        const int sa = gen_slot[i] < NA ? gen_slot[i] : na - 1;
+        const float *srow = reinterpret_cast<const float *>(&stab[par][0][sa][0]) + c * 8;
+        const float *irow = reinterpret_cast<const float *>(&stab[par][1][sa][0]) + c * 8;
+        float v[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const f32x8 s8 = *reinterpret_cast<const f32x8 *>(srow + ks * 32);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[ks][e] = wg[ks][e] * s8[e];
+        }
+        build_tile<TOp, KS, ASYM, EXACT>(v, levels, maxq, inv_levels, inv_maxq, irow,
+                                         &dbuf[par][gen_slot[i]][0][lane]);
+    };
+    auto build = [&](auto exm_tag, const V8in (&wraw)[KS], int par) {
+        constexpr int EXM = decltype(exm_tag)::value;
+        float wg[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            widen8<TIn>(wraw[ks], wg[ks]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                wg[ks][e] = row_ok ? wg[ks][e] : 0.f;
+        }
+        build_slot(std::integral_constant<bool, (EXM >= 1)>{}, wg, par, 0);
+#pragma unroll
+        for (int i = 1; i < GPW; ++i)
+            if (i < gen_n)
+                build_slot(std::integral_constant<bool, (EXM == 2)>{}, wg, par, i);
+    };
 
     f32x4 acc[NA][kTT];
 #pragma unroll
@@ -201,113 +422,92 @@ __global__ __launch_bounds__(256, 1) void k_search(
         for (int tt = 0; tt < kTT; ++tt)
             acc[a][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const V8 zero8 = {};
-    for (int i = threadIdx.x; i < (NA - na) * KS * 64; i += blockDim.x)
-        (&dtile[na][0][0])[i] = zero8;
-
-    for (int64_t k0 = 0; k0 < in; k0 += G) {
-        // X fragments of this wave's 64 tokens (A operand), reused by every candidate.
-        // Tokens past the end read the last token's row (always in bounds)
-        // and are replaced by zeros, so they add nothing to the error.
-        V8 xa[kTT][KS];
+    const int64_t ngroups = in / G;
+    const int64_t glast = ngroups - 1;
+    // MFMAs of all NA candidates of the group whose tiles are in buffer par.
+    // Every slot, unconditionally: a branch around an MFMA would make its
+    // accumulator a control-flow merge, which the compiler resolves by
+    // copying all accumulators between register files. Slots past na hold
+    // valid but unused tiles and are never read out. The B fragments of
+    // candidate a+1 are read before the MFMAs of candidate a (pinned, so the
+    // LDS latency hides under the MFMAs).
+    auto mfma_group = [&](int par) {
+        V8 bcur[KS];
 #pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) {
-            const int64_t t = tok0 + tt * 16 + r;
-            const int64_t tc = t < tokens ? t : tokens - 1;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const V8 x = ToOp<TIn, TOp>::run(load8(X + tc * in + k0 + ks * 32 + c * 8));
-                xa[tt][ks] = t < tokens ? x : zero8;
-            }
-        }
-        // This lane's weights: row `row`, columns k0 + 32 ks + 8 c + (0..7);
-        // rows past the end are zero (their D is zero and adds nothing).
-        float w[KS][8];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            widen8<TIn>(load8(W + row_c * in + k0 + ks * 32 + c * 8), w[ks]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                w[ks][i] = row_ok ? w[ks][i] : 0.f;
-        }
-
-        // Build the D tiles of this wave's candidates.
-        for (int a = wave; a < na; a += kWaves) {
-            const float *srow = s_tab + (int64_t)(a0 + a) * in + k0 + c * 8;
-            const float *irow = inv_tab + (int64_t)(a0 + a) * in + k0 + c * 8;
-            float v[KS][8];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const f32x8 s8 = *reinterpret_cast<const f32x8 *>(srow + ks * 32);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    v[ks][i] = w[ks][i] * s8[i];
-            }
-            float scale, rs, zlo = 0.f, zhi = 0.f;
-            if (mode == AWQ_SYM) {
-                float m = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        m = fmaxf(m, fabsf(v[ks][i]));
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
-                scale = fmaxf(m / levels, 1e-8f);
-                rs = 1.0f / scale;
-                zlo = -levels - 1.0f;
-                zhi = levels;
-            } else {
-                float lo = 0.f, hi = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        lo = fminf(lo, v[ks][i]);
-                        hi = fmaxf(hi, v[ks][i]);
-                    }
-                lo = fminf(lo, __shfl_xor(lo, 16));
-                lo = fminf(lo, __shfl_xor(lo, 32));
-                hi = fmaxf(hi, __shfl_xor(hi, 16));
-                hi = fmaxf(hi, __shfl_xor(hi, 32));
-                scale = fmaxf((hi - lo) / maxq, 1e-8f);
-                rs = 1.0f / scale;
-                const float zero = rintf(-lo / scale);
-                zlo = -zero;
-                zhi = maxq - zero;
-            }
-            V8 *dst = &dtile[a][0][lane];
-            const bool exact = unit[a0 + a] != 0;
-            if (mode == AWQ_SYM) {
-                if (exact)
-                    emit_tile<TOp, KS, false, true>(v, scale, rs, zlo, zhi, irow, dst);
-                else
-                    emit_tile<TOp, KS, false, false>(v, scale, rs, zlo, zhi, irow, dst);
-            } else {
-                if (exact)
-                    emit_tile<TOp, KS, true, true>(v, scale, rs, zlo, zhi, irow, dst);
-                else
-                    emit_tile<TOp, KS, true, false>(v, scale, rs, zlo, zhi, irow, dst);
-            }
-        }
-        __syncthreads();
-
-        // Unconditional over all NA slots: a branch around an MFMA would make
-        // its accumulator a control-flow merge, which the compiler resolves
-        // by copying every accumulator out of and back into AGPRs each group.
-        // Slots >= na hold zero tiles (cleared once below) and are never read out.
+        for (int ks = 0; ks < KS; ++ks)
+            bcur[ks] = dbuf[par][0][ks][lane];
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
+            V8 bnext[KS];
+            if (a + 1 < NA)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const V8 b = dtile[a][ks][lane];
+                for (int ks = 0; ks < KS; ++ks)
+                    bnext[ks] = dbuf[par][a + 1][ks][lane];
+            // Each accumulator's MFMAs back to back: with the column steps
+            // interleaved instead, the register allocator permutes the
+            // loop-carried accumulators every group.
 #pragma unroll
-                for (int tt = 0; tt < kTT; ++tt)
-                    acc[a][tt] = Mfma<TOp>::run(xa[tt][ks], b, acc[a][tt]);
-            }
+            for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc[a][tt] = Mfma<TOp>::run(xa[tt][ks], bcur[ks], acc[a][tt]);
+            if (a + 1 < NA)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    bcur[ks] = bnext[ks];
         }
-        __syncthreads();
-    }
+        __builtin_amdgcn_sched_group_barrier(0x0100, KS, 0);
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            if (a + 1 < NA)
+                __builtin_amdgcn_sched_group_barrier(0x0100, KS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x0008, KS * kTT * MfmaCount<TOp>::value, 0);
+        }
+    };
+
+    // One iteration per group g, one barrier each: the MFMAs of group g
+    // (tiles in buffer g & 1), then the building of group g+1's tiles into
+    // the other buffer.
+    auto run = [&](auto exm_tag) {
+        {
+            f32x4 sv[kSPer];
+            fetch_s(0, sv);
+            store_s(0, sv);
+            fetch_s(ngroups > 1 ? 1 : 0, sv);
+            store_s(1, sv);
+        }
+        {
+            V8in w0[KS];
+            load_w(0, w0);
+            load_x(0, xa);
+            __syncthreads();
+            build(exm_tag, w0, 0);
+        }
+        for (int64_t g = 0; g < ngroups; ++g) {
+            const int par = (int)(g & 1);
+            // Next group's weights and the s rows of the group after it are
+            // fetched first; the next group's X fragments after this group's
+            // MFMAs, so the current and next fragments are never live
+            // together. (The last groups reload valid groups; what they then
+            // build or store lands in buffers nobody reads again.)
+            const int64_t gn = g + 1 < ngroups ? g + 1 : glast;
+            V8in wn[KS];
+            load_w(gn * G, wn);
+            f32x4 sv[kSPer];
+            fetch_s(g + 2 < ngroups ? g + 2 : glast, sv);
+            __syncthreads();
+            mfma_group(par);
+            load_x(gn * G, xa);
+            build(exm_tag, wn, par ^ 1);
+            store_s(par, sv);
+        }
+    };
+    if (exm == 0)
+        run(std::integral_constant<int, 0>{});
+    else if (exm == 1)
+        run(std::integral_constant<int, 1>{});
+    else
+        run(std::integral_constant<int, 2>{});
 
     // Sum of squares: exact fp64 squares of the fp32 accumulators, fixed order.
 #pragma unroll
@@ -331,7 +531,10 @@ __global__ __launch_bounds__(256, 1) void k_search(
     __syncthreads();
     if ((int)threadIdx.x < na) {
         const int a = threadIdx.x;
-        const double total = ((wsum[0][a] + wsum[1][a]) + wsum[2][a]) + wsum[3][a];
+        double total = wsum[0][a];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            total += wsum[w][a];
         partial[(int64_t)(a0 + a) * nblk + blk] = total;
     }
 }
@@ -394,9 +597,14 @@ static hipError_t search_typed(const void *W, const void *X, int64_t out, int64_
     constexpr int NA = SearchShape<TOp, G>::NA;
     dim3 grid((unsigned)((out + 15) / 16), (unsigned)((tokens + kTokPerBlock - 1) / kTokPerBlock),
               (unsigned)((n_alpha + NA - 1) / NA));
-    hipLaunchKernelGGL((k_search<TIn, TOp, G>), grid, dim3(256), 0, st, (const TIn *)W,
-                       (const TIn *)X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, mode,
-                       partial);
+    if (mode == AWQ_SYM)
+        hipLaunchKernelGGL((k_search<TIn, TOp, G, false>), grid, dim3(kWaves * 64), 0, st, (const TIn *)W,
+                           (const TIn *)X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits,
+                           partial);
+    else
+        hipLaunchKernelGGL((k_search<TIn, TOp, G, true>), grid, dim3(kWaves * 64), 0, st, (const TIn *)W,
+                           (const TIn *)X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits,
+                           partial);
     return hipGetLastError();
 }
 
