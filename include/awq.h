@@ -58,7 +58,9 @@ enum {
  * chunks, then the chunk sums in ascending chunk order; bitwise reproducible.
  *   X:    device, (tokens, in) of `dtype`.
  *   xmag: device, fp32[in] (output).
- *   ws:   device scratch of at least awq_act_stats_workspace_size(tokens, in) bytes.
+ *   ws:   device scratch of awq_act_stats_workspace_size(tokens, in) bytes; the
+ *         current kernel keeps its partial sums on chip, the size is 0 and ws
+ *         may be NULL (the argument stays for kernels that need scratch).
  */
 int awq_act_stats(const void *X, int dtype, int64_t tokens, int64_t in, float *xmag,
                   void *ws, size_t ws_bytes, void *stream);

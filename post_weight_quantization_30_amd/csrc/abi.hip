@@ -19,12 +19,6 @@ bool pack_group_ok(int g)
     return g == 32 || g == 64 || g == 128 || g == 256 || g == 512 || g == 1024 || g == 2048;
 }
 
-size_t stats_ws_bytes(int64_t tokens, int64_t in)
-{
-    const int64_t nchunk = (tokens + 63) / 64;
-    return (size_t)(nchunk * in) * sizeof(double);
-}
-
 }  // namespace
 
 extern "C" {
@@ -44,9 +38,9 @@ const char *awq_status_string(int status)
 
 size_t awq_act_stats_workspace_size(int64_t tokens, int64_t in)
 {
-    if (tokens < 1 || in < 1)
-        return 0;
-    return stats_ws_bytes(tokens, in);
+    (void)tokens;
+    (void)in;
+    return 0;   // the statistics kernel keeps its partial sums in LDS
 }
 
 int awq_act_stats(const void *X, int dtype, int64_t tokens, int64_t in, float *xmag, void *ws,
@@ -54,16 +48,19 @@ int awq_act_stats(const void *X, int dtype, int64_t tokens, int64_t in, float *x
 {
     if (!X || !xmag || tokens < 1 || in < 1 || !valid_dtype(dtype))
         return AWQ_ERR_INVALID_ARG;
-    if (!ws || ws_bytes < stats_ws_bytes(tokens, in))
-        return AWQ_ERR_WORKSPACE;
-    return hip_status(awq::launch_act_stats(X, dtype, tokens, in, xmag, (double *)ws,
-                                            (hipStream_t)stream));
+    (void)ws;
+    (void)ws_bytes;
+    if ((in + 63) / 64 > (int64_t)0x7fffffff)
+        return AWQ_ERR_UNSUPPORTED;
+    return hip_status(awq::launch_act_stats(X, dtype, tokens, in, xmag, (hipStream_t)stream));
 }
 
 int awq_s_table(const float *xmag, int64_t in, int grid, float *s_table, void *stream)
 {
     if (!xmag || !s_table || in < 1 || grid < 1 || grid > AWQ_MAX_GRID)
         return AWQ_ERR_INVALID_ARG;
+    if ((in + 255) / 256 > (int64_t)0x7fffffff)
+        return AWQ_ERR_UNSUPPORTED;
     return hip_status(awq::launch_s_table(xmag, in, grid, s_table, nullptr, nullptr,
                                           (hipStream_t)stream));
 }
@@ -90,7 +87,8 @@ int check_workspace(int64_t out, int64_t in, int64_t tokens, int grid, const voi
     *lay = awq::search_ws_layout(out, in, tokens, grid);
     if (!ws || ws_bytes < lay->total)
         return AWQ_ERR_WORKSPACE;
-    if (lay->nblk > (int64_t)0x7fffffff || (tokens + awq::kTokPerBlock - 1) / awq::kTokPerBlock > 65535)
+    if (lay->nblk > (int64_t)0x7fffffff || (tokens + awq::kTokPerBlock - 1) / awq::kTokPerBlock > 65535 ||
+        (in + 255) / 256 > (int64_t)0x7fffffff)
         return AWQ_ERR_UNSUPPORTED;
     return AWQ_OK;
 }

@@ -71,7 +71,7 @@ inline SearchWs search_ws_layout(int64_t out, int64_t in, int64_t tokens, int gr
 
 // Launchers (each returns the first HIP error, hipSuccess otherwise).
 hipError_t launch_act_stats(const void *X, int dtype, int64_t tokens, int64_t in, float *xmag,
-                            double *partial, hipStream_t st);
+                            hipStream_t st);
 hipError_t launch_s_table(const float *xmag, int64_t in, int grid, float *s_tab, float *inv_tab,
                           int32_t *unit, hipStream_t st);
 hipError_t launch_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,

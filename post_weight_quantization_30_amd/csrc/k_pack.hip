@@ -9,8 +9,9 @@
 //   and rtn under "GPTQ: compensate the error you just made"):
 //     lo = min(min v, 0), hi = max(max v, 0), scale = max((hi - lo) / maxq, 1e-8),
 //     zero = rne(-lo / scale), code = clamp(rne(v / scale) + zero, 0, maxq)
-// Divisions are IEEE (hipcc's default correctly rounded fp32 division), the
-// library is built with -ffp-contract=off and rintf is v_rndne_f32.
+// Every quotient is the correctly rounded one (an IEEE division per group for
+// the reciprocal, two fma residual steps per weight), the library is built
+// with -ffp-contract=off and rintf is v_rndne_f32.
 //
 // Layout: one lane owns 32 consecutive columns of one row. 32 codes of b bits
 // fill exactly b 32-bit words, so a lane writes whole words of the row's
@@ -20,6 +21,7 @@
 // write b/8 B per weight plus 5 B per group.
 #include "awq_internal.h"
 
+#include <float.h>
 #include <math.h>
 
 namespace awq {
@@ -42,6 +44,43 @@ __device__ __forceinline__ void pack_store(const uint32_t (&code)[32], uint32_t 
 #pragma unroll
     for (int k = 0; k < BITS; ++k)
         dst[k] = word[k];
+}
+
+// a / b rounded to nearest even, for finite b >= 1e-8 and y = a correctly
+// rounded 1/b (an IEEE division, once per group). q0 = a*y is within 2 ulp of
+// a/b; one residual step (the residual a - b*q is exact or nearly so in an
+// fma) makes it faithful, and a second one, with a faithful q and a correctly
+// rounded y, gives the correctly rounded quotient (Markstein's theorem).
+// Quotients small enough for the residual to underflow lie far below 0.5 and
+// round to the same integer either way.
+__device__ __forceinline__ float div_rn(float a, float b, float y)
+{
+    float q = a * y;
+    q = fmaf(fmaf(-b, q, a), y, q);
+    return fmaf(fmaf(-b, q, a), y, q);
+}
+
+// codes of one lane's 32 values: clamp(rne(v / scale) + zero, lo, hi) for
+// asymmetric, clamp(rne(v / scale), lo, hi) + zero for symmetric. FAST uses
+// div_rn (finite scale), otherwise the IEEE division (infinite scale, where
+// the residual steps would turn 0 * inf into NaN).
+template <bool ASYM, bool FAST>
+__device__ __forceinline__ void codes(const float (&v)[32], float scale, float lo, float hi, float zero,
+                                      uint32_t (&code)[32])
+{
+    const float y = FAST ? 1.0f / scale : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float u = FAST ? div_rn(v[i], scale, y) : v[i] / scale;
+        float q = rintf(u);
+        if (ASYM) {
+            q = fminf(fmaxf(q + zero, lo), hi);
+            code[i] = (uint32_t)(int)q;
+        } else {
+            q = fminf(fmaxf(q, lo), hi);
+            code[i] = (uint32_t)((int)q + (int)zero);
+        }
+    }
 }
 
 template <typename T>
@@ -89,12 +128,10 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
             m = fmaxf(m, __shfl_xor(m, off));
         scale = fmaxf(m / levels, 1e-8f);
         zero = (float)(1 << (bits - 1));
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            float q = rintf(v[i] / scale);
-            q = fminf(fmaxf(q, -levels - 1.0f), levels);
-            code[i] = (uint32_t)((int)q + (1 << (bits - 1)));
-        }
+        if (scale <= FLT_MAX)
+            codes<false, true>(v, scale, -levels - 1.0f, levels, zero, code);
+        else
+            codes<false, false>(v, scale, -levels - 1.0f, levels, zero, code);
     } else {
         const float maxq = (float)((1 << bits) - 1);
         float lo = 0.f, hi = 0.f;
@@ -109,12 +146,10 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
         }
         scale = fmaxf((hi - lo) / maxq, 1e-8f);
         zero = rintf(-lo / scale);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            float q = rintf(v[i] / scale) + zero;
-            q = fminf(fmaxf(q, 0.0f), maxq);
-            code[i] = (uint32_t)(int)q;
-        }
+        if (scale <= FLT_MAX)
+            codes<true, true>(v, scale, 0.0f, maxq, zero, code);
+        else
+            codes<true, false>(v, scale, 0.0f, maxq, zero, code);
     }
     if (!active)
         return;

@@ -12,23 +12,23 @@
 //    D = (q*scale - v) / s with v = w*s, built in registers from the group
 //    statistics and converted once (round-to-nearest-even) to the MFMA
 //    operand type.
-//  * One block = 16 output rows x 256 tokens x up to NA candidates, 4 waves.
-//    The error needs the full-K sum of X D^T before squaring, so K cannot be
-//    split: every candidate keeps its own fp32 accumulator tile
-//    (NA x 4 tiles x 4 values = 336 registers per lane at NA = 21), which is
-//    what limits the block to 16 rows x 256 tokens.
-//  * Per group of G input columns: each wave builds the D tiles of its share
-//    of the candidates (wave w takes candidates w, w+4, ...) in the exact
-//    register layout of the MFMA B operand and stores them to LDS; after a
-//    barrier every wave runs the 16x16x32 MFMAs of all candidates against its
-//    own 64 tokens, whose X fragments stay in registers across candidates.
-//    D is therefore generated once per (row, column, candidate) and reused by
-//    all 256 tokens of the block.
+//  * One block = 16 output rows x 256 tokens x up to NA = 11 candidates,
+//    8 waves (two per SIMD), 32 tokens each. The error needs the full-K sum
+//    of X D^T before squaring, so K cannot be split: every candidate keeps
+//    its own fp32 accumulator tile (NA x 2 tiles x 4 values = 88 registers
+//    per lane), which is what limits the block to 16 rows x 256 tokens x 11
+//    candidates; 21 candidates take two blocks.
+//  * Per group of G input columns: each wave builds the D tiles of one or
+//    two candidates in the exact register layout of the MFMA B operand and
+//    stores them to LDS; after a barrier every wave runs the 16x16x32 MFMAs
+//    of all candidates against its own 32 tokens, whose X fragments stay in
+//    registers across candidates. D is therefore generated once per (row,
+//    column, candidate) and reused by all 256 tokens of the block.
 //  * The group maximum (or min/max) of a row is in-lane over KS*8 values plus
 //    two cross-lane steps: lanes r, r+16, r+32, r+48 hold the 4 column slices
 //    of row r.
 //  * Epilogue: squares summed in fp64 per lane, then a fixed butterfly per
-//    wave and a fixed-order sum of the 4 waves: one fp64 partial per
+//    wave and a fixed-order sum of the 8 waves: one fp64 partial per
 //    (candidate, block); no atomics, so results are bitwise reproducible.
 //  * The search may round differently from the exact quantizer (a reciprocal
 //    multiply instead of the IEEE division, contracted multiply-adds, 16-bit
@@ -90,6 +90,22 @@ __device__ __forceinline__ float lanes4_min(float m)
     m = fminf(__int_as_float(a[0]), __int_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
     return fminf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+
+// fp32(w * s) for a stored fp16 weight, the low or high half of a 32-bit
+// pair, in one instruction: v_fma_mix_f32 widens an fp16 source exactly and
+// rounds w * s + 0 once (the same value as widening and multiplying).
+__device__ __forceinline__ float mul_f16_lo(uint32_t pair, float s)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(s));
+    return r;
+}
+__device__ __forceinline__ float mul_f16_hi(uint32_t pair, float s)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(s));
+    return r;
 }
 
 // MFMA instructions per 32-column step of one 16x16 tile.
@@ -242,22 +258,22 @@ __device__ __forceinline__ void build_tile(const float (&v)[KS][8], float levels
 }
 
 // One block: 16 output rows x 256 tokens x NA candidates (candidates a0 ..
-// a0 + NA - 1, a0 = NA * blockIdx.z), 4 waves, one wave per SIMD (the 16 * NA
-// accumulator registers per lane leave room for nothing else on the SIMD).
+// a0 + NA - 1, a0 = NA * blockIdx.z), 8 waves of 32 tokens, two per SIMD.
 //
 // Software pipeline over groups of G input columns, one barrier per group:
 // the D tiles live in two LDS buffers selected by group parity. In the
 // iteration of group g every wave
-//   1. issues the loads of group g+1's X fragments and weights (registers),
+//   1. issues the loads of group g+1's weights and of group g+2's s rows,
 //   2. waits at the barrier (group g's tiles are complete; group g-1's have
 //      been read by everyone),
 //   3. runs the MFMAs of all NA candidates of group g (B fragments read one
-//      candidate ahead),
-//   4. builds its share of group g+1's tiles (wave w: candidates w, w+4, ...)
-//      into the other buffer.
-// On gfx950 a wave's MFMA and VALU time add up rather than overlap, so the
-// pipeline's job is to keep LDS and global-memory latency off the critical
-// path, not to hide the VALU work.
+//      candidate ahead), then issues the loads of group g+1's X fragments,
+//   4. builds its share of group g+1's tiles into the other buffer and
+//      stages group g+2's s rows.
+// Measured on gfx950, a SIMD's MFMA and VALU time add up rather than overlap
+// (also across waves, and also with waves specialised to one of the two
+// roles), so the time per group is close to the MFMA time plus the tile
+// generation's VALU time; the pipeline keeps LDS and memory latency out of it.
 template <typename TIn, typename TOp, int G, bool ASYM>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     const TIn *__restrict__ W, const TIn *__restrict__ X, int64_t out, int64_t in, int64_t tokens,
@@ -294,15 +310,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     const float inv_levels = 1.0f / levels;
     const float inv_maxq = 1.0f / maxq;
 
-    // X rows of this wave's tokens, clamped to the last token (always in
-    // bounds); tokens past the end are zeroed after the load.
+    // X rows of this wave's tokens and the W row of this lane, clamped to the
+    // last token / row (always in bounds). The products of the clamped
+    // duplicates land in accumulator entries of tokens or rows past the end,
+    // which the epilogue leaves out; nothing is masked inside the loop.
     const TIn *xrow[kTT];
-    bool tok_ok[kTT];
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
         const int64_t t = tok0 + tt * 16 + r;
-        tok_ok[tt] = t < tokens;
-        xrow[tt] = X + (tok_ok[tt] ? t : tokens - 1) * in + c * 8;
+        xrow[tt] = X + (t < tokens ? t : tokens - 1) * in + c * 8;
     }
     const TIn *wrow = W + row_c * in + c * 8;
 
@@ -331,10 +347,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     // group loop, so each loop body is free of per-tile branches.
     const bool all_unit = unit[n_alpha - 1] != 0;
     const int exm = all_unit ? 2 : (a0 == 0 && gen_slot[0] == 0 ? 1 : 0);
-    // Waves whose 64 tokens are all in range never touch their X fragments
-    // between load and MFMA, so the loads' latency stays hidden.
-    const bool tok_full = tok0 + kTokPerWave <= tokens;
-
     V8 xa[kTT][KS];
     auto load_x = [&](int64_t k0, V8 (&xd)[kTT][KS]) {
 #pragma unroll
@@ -342,14 +354,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 xd[tt][ks] = ToOp<TIn, TOp>::run(load8(xrow[tt] + k0 + ks * 32));
-        if (!tok_full) {
-            const V8 zero8 = {};
-#pragma unroll
-            for (int tt = 0; tt < kTT; ++tt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    xd[tt][ks] = tok_ok[tt] ? xd[tt][ks] : zero8;
-        }
     };
     auto load_w = [&](int64_t k0, V8in (&wd)[KS]) {
 #pragma unroll
@@ -382,7 +386,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
                 (&stab[sp][0][0][0])[e] = sv[i];
         }
     };
-    auto build_slot = [&](auto exact_tag, const float (&wg)[KS][8], int par, int i) {
+    // v = w * s of one candidate: fp16 weights straight from the loaded
+    // pairs (v_fma_mix_f32), other types from the once-widened wg.
+    auto build_slot = [&](auto exact_tag, const V8in (&wraw)[KS], const float (&wg)[KS][8], int par,
+                          int i) {
         constexpr bool EXACT = decltype(exact_tag)::value;
         const int sa = gen_slot[i] < NA ? gen_slot[i] : na - 1;
         const float *srow = reinterpret_cast<const float *>(&stab[par][0][sa][0]) + c * 8;
@@ -391,9 +398,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const f32x8 s8 = *reinterpret_cast<const f32x8 *>(srow + ks * 32);
+            if constexpr (std::is_same<TIn, f16>::value) {
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 pr = __builtin_bit_cast(u32x4, wraw[ks]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[ks][e] = wg[ks][e] * s8[e];
+                for (int e = 0; e < 4; ++e) {
+                    v[ks][2 * e] = mul_f16_lo(pr[e], s8[2 * e]);
+                    v[ks][2 * e + 1] = mul_f16_hi(pr[e], s8[2 * e + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[ks][e] = wg[ks][e] * s8[e];
+            }
         }
         build_tile<TOp, KS, ASYM, EXACT>(v, levels, maxq, inv_levels, inv_maxq, irow,
                                          &dbuf[par][gen_slot[i]][0][lane]);
@@ -401,18 +418,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     auto build = [&](auto exm_tag, const V8in (&wraw)[KS], int par) {
         constexpr int EXM = decltype(exm_tag)::value;
         float wg[KS][8];
+        if constexpr (!std::is_same<TIn, f16>::value) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            widen8<TIn>(wraw[ks], wg[ks]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                wg[ks][e] = row_ok ? wg[ks][e] : 0.f;
+            for (int ks = 0; ks < KS; ++ks)
+                widen8<TIn>(wraw[ks], wg[ks]);
         }
-        build_slot(std::integral_constant<bool, (EXM >= 1)>{}, wg, par, 0);
+        build_slot(std::integral_constant<bool, (EXM >= 1)>{}, wraw, wg, par, 0);
 #pragma unroll
         for (int i = 1; i < GPW; ++i)
             if (i < gen_n)
-                build_slot(std::integral_constant<bool, (EXM == 2)>{}, wg, par, i);
+                build_slot(std::integral_constant<bool, (EXM == 2)>{}, wraw, wg, par, i);
     };
 
     f32x4 acc[NA][kTT];
@@ -510,6 +525,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
         run(std::integral_constant<int, 2>{});
 
     // Sum of squares: exact fp64 squares of the fp32 accumulators, fixed order.
+    // Lane l holds, of tile tt, output row r = l & 15 for the tokens
+    // tok0 + 16 tt + 4 (l >> 4) + e; entries of rows or tokens past the end
+    // (products of the clamped duplicates) are left out.
+    bool keep[kTT][4];
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            keep[tt][e] = row_ok && tok0 + tt * 16 + 4 * c + e < tokens;
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
         if (a < na) {
@@ -518,7 +542,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
             for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const double x = (double)acc[a][tt][e];
+                    const double x = keep[tt][e] ? (double)acc[a][tt][e] : 0.0;
                     sum += x * x;
                 }
 #pragma unroll
@@ -539,54 +563,62 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     }
 }
 
-// Per candidate: fixed-order reduction of the block partials (each thread a
-// contiguous stretch, then a fixed tree), mse = sse / (tokens * out).
-__global__ __launch_bounds__(256) void k_reduce(const double *__restrict__ partial, int64_t nblk,
-                                               double denom, double *__restrict__ mse)
-{
-    __shared__ double buf[256];
-    const int a = blockIdx.x;
-    const int64_t per = (nblk + 255) / 256;
-    const int64_t b0 = threadIdx.x * per;
-    const int64_t b1 = b0 + per < nblk ? b0 + per : nblk;
-    double s = 0.0;
-    for (int64_t b = b0; b < b1; ++b)
-        s += partial[(int64_t)a * nblk + b];
-    buf[threadIdx.x] = s;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-        if ((int)threadIdx.x < h)
-            buf[threadIdx.x] += buf[threadIdx.x + h];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0)
-        mse[a] = buf[0] / denom;
-}
+// The finish: fixed-order reduction of the block partials of every candidate
+// (wave w takes candidates w, w + 16, ...; lane l sums partials l, l + 64, ...
+// in order, then a fixed xor butterfly), then the first strict minimum over
+// the candidates (a NaN never compares below) and s_best = that row of the
+// s-table, or all ones when nothing is finite. One block: the work is a few
+// thousand doubles for the layers this is meant for.
+constexpr int kFinishWaves = 16;
 
-// First strict minimum over the candidates (a NaN never compares below), then
-// s_best = that row of the s-table, or all ones when nothing is finite.
-__global__ __launch_bounds__(1024) void k_argmin(const double *__restrict__ mse, int n_alpha,
-                                                 const float *__restrict__ s_tab, int64_t in,
-                                                 int32_t *__restrict__ best, float *__restrict__ s_best)
+__global__ __launch_bounds__(kFinishWaves * 64) void k_finish(const double *__restrict__ partial,
+                                                            int64_t nblk, int n_alpha, double denom,
+                                                            const float *__restrict__ s_tab,
+                                                            int64_t in, double *__restrict__ mse,
+                                                            int32_t *__restrict__ best,
+                                                            float *__restrict__ s_best)
 {
+    __shared__ double err[AWQ_MAX_GRID + 1];
     __shared__ int sbest;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int a = wave; a < n_alpha; a += kFinishWaves) {
+        const double *p = partial + (int64_t)a * nblk;
+        double acc = 0.0;
+        int64_t b = lane;
+        for (; b + 192 < nblk; b += 256) {
+            const double x0 = p[b], x1 = p[b + 64], x2 = p[b + 128], x3 = p[b + 192];
+            acc += x0;
+            acc += x1;
+            acc += x2;
+            acc += x3;
+        }
+        for (; b < nblk; b += 64)
+            acc += p[b];
+        for (int off = 32; off > 0; off >>= 1)
+            acc += __shfl_xor(acc, off);
+        if (lane == 0) {
+            const double m = acc / denom;
+            err[a] = m;
+            mse[a] = m;
+        }
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        int b = -1;
+        int bi = -1;
         double be = INFINITY;
         for (int k = 0; k < n_alpha; ++k) {
-            const double e = mse[k];
-            if (e < be) {
-                be = e;
-                b = k;
+            if (err[k] < be) {
+                be = err[k];
+                bi = k;
             }
         }
-        sbest = b;
-        *best = b;
+        sbest = bi;
+        *best = bi;
     }
     __syncthreads();
-    const int b = sbest;
+    const int bi = sbest;
     for (int64_t j = threadIdx.x; j < in; j += blockDim.x)
-        s_best[j] = b >= 0 ? s_tab[(int64_t)b * in + j] : 1.0f;
+        s_best[j] = bi >= 0 ? s_tab[(int64_t)bi * in + j] : 1.0f;
 }
 
 template <typename TIn, typename TOp, int G>
@@ -659,13 +691,8 @@ hipError_t launch_reduce_argmin(const double *partial, int64_t nblk, int n_alpha
                                 int64_t tokens, int64_t in, const float *s_tab, double *mse,
                                 int32_t *best, float *s_best, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_reduce, dim3((unsigned)n_alpha), dim3(256), 0, st, partial, nblk,
-                       (double)tokens * (double)out, mse);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(k_argmin, dim3(1), dim3(1024), 0, st, (const double *)mse, n_alpha, s_tab,
-                       in, best, s_best);
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinishWaves * 64), 0, st, partial, nblk, n_alpha,
+                       (double)tokens * (double)out, s_tab, in, mse, best, s_best);
     return hipGetLastError();
 }
 

@@ -6,156 +6,150 @@
 // Step 2 (same page, "The code, line by line"): alpha_k = k / grid,
 //   s[k][j] = fp32(xmag[j]^alpha_k / sqrt(max_j xmag^alpha_k * min_j xmag^alpha_k)).
 //
-// Both are HBM/latency bound and tiny next to the search; the design goal is
-// a bitwise-reproducible result, not speed: the sum order is fixed (sequential
-// inside 64-token chunks, then the chunk sums in ascending order) and every
+// Both are tiny next to the search; besides speed the goal is a bitwise
+// reproducible result: the sum order is fixed (sequential inside 64-token
+// chunks, then the chunk sums in ascending order, starting from 0) and every
 // fp64 operation is a single IEEE operation (the library is built with
 // -ffp-contract=off).
 #include "awq_internal.h"
 
+#include <float.h>
 #include <math.h>
 
 namespace awq {
 
-constexpr int kChunk = 64;   // tokens per fixed-order partial sum
+constexpr int kChunk = 64;        // tokens per fixed-order partial sum
+constexpr int kStatWaves = 16;    // chunks summed at once by one block
 
-// One thread owns V adjacent columns of one 64-token chunk and sums them in
-// token order. Consecutive threads own consecutive columns, so every token row
-// is read with contiguous, coalesced loads.
-template <typename T, int V>
-__global__ __launch_bounds__(256) void k_act_partial(const T *__restrict__ X, int64_t tokens,
-                                                      int64_t in, double *__restrict__ partial)
+// One block owns 64 adjacent columns (one per lane) and up to 16 waves; in
+// round r wave w sums chunk r*waves + w of its lane's column, with all 64
+// loads of a full chunk issued before the sequential adds (one memory round
+// trip per chunk). Wave 0 then adds the round's chunk sums, in chunk order, to
+// the running total. Rows of X are read 64 columns at a time, coalesced.
+template <typename T>
+__global__ __launch_bounds__(kStatWaves * 64) void k_act_stats(const T *__restrict__ X,
+                                                                int64_t tokens, int64_t in,
+                                                                float *__restrict__ xmag)
 {
-    const int64_t j0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
-    const int64_t c = blockIdx.y;
-    if (j0 >= in)
-        return;
-    const int64_t t0 = c * kChunk;
-    const int64_t t1 = t0 + kChunk < tokens ? t0 + kChunk : tokens;
-    double acc[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-        acc[v] = 0.0;
-    if (j0 + V <= in) {
-        struct alignas(sizeof(T) * V) Pack { T e[V]; };
-        for (int64_t t = t0; t < t1; ++t) {
-            const Pack p = *reinterpret_cast<const Pack *>(X + t * in + j0);
-#pragma unroll
-            for (int v = 0; v < V; ++v)
-                acc[v] += fabs((double)static_cast<float>(p.e[v]));
-        }
-    } else {
-        for (int64_t t = t0; t < t1; ++t)
-            for (int v = 0; v < V && j0 + v < in; ++v)
-                acc[v] += fabs((double)static_cast<float>(X[t * in + j0 + v]));
-    }
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-        if (j0 + v < in)
-            partial[c * in + j0 + v] = acc[v];
-}
-
-__global__ __launch_bounds__(256) void k_act_finalize(const double *__restrict__ partial,
-                                                       int64_t nchunk, int64_t tokens, int64_t in,
-                                                       float *__restrict__ xmag)
-{
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= in)
-        return;
+    __shared__ double csum[kStatWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int waves = blockDim.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+    const bool col_ok = j < in;
+    const int64_t jc = col_ok ? j : in - 1;   // in-bounds column for idle lanes
+    const int64_t nchunk = (tokens + kChunk - 1) / kChunk;
     double total = 0.0;
-    for (int64_t c = 0; c < nchunk; ++c)
-        total += partial[c * in + j];
-    const double mean = total / (double)tokens;
-    xmag[j] = (float)(mean + 1e-8);
+    for (int64_t c0 = 0; c0 < nchunk; c0 += waves) {
+        const int64_t c = c0 + wave;
+        double acc = 0.0;
+        if (c < nchunk) {
+            const int64_t t0 = c * kChunk;
+            const T *p = X + t0 * in + jc;
+            if (t0 + kChunk <= tokens) {
+                float v[kChunk];
+#pragma unroll
+                for (int t = 0; t < kChunk; ++t)
+                    v[t] = static_cast<float>(p[(int64_t)t * in]);
+#pragma unroll
+                for (int t = 0; t < kChunk; ++t)
+                    acc += fabs((double)v[t]);
+            } else {
+                for (int64_t t = t0; t < tokens; ++t, p += in)
+                    acc += fabs((double)static_cast<float>(*p));
+            }
+        }
+        csum[wave][lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            const int64_t nr = nchunk - c0 < waves ? nchunk - c0 : waves;
+            for (int w = 0; w < nr; ++w)
+                total += csum[w][lane];
+        }
+        __syncthreads();
+    }
+    if (wave == 0 && col_ok)
+        xmag[j] = (float)(total / (double)tokens + 1e-8);
 }
 
-template <typename T, int V>
-static hipError_t stats_typed(const T *X, int64_t tokens, int64_t in, float *xmag, double *partial,
-                              hipStream_t st)
+template <typename T>
+static hipError_t stats_typed(const T *X, int64_t tokens, int64_t in, float *xmag, hipStream_t st)
 {
     const int64_t nchunk = (tokens + kChunk - 1) / kChunk;
-    const int64_t threads = (in + V - 1) / V;
-    dim3 grid((unsigned)((threads + 255) / 256), (unsigned)nchunk);
-    hipLaunchKernelGGL((k_act_partial<T, V>), grid, dim3(256), 0, st, X, tokens, in, partial);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(k_act_finalize, dim3((unsigned)((in + 255) / 256)), dim3(256), 0, st,
-                       (const double *)partial, nchunk, tokens, in, xmag);
+    const int waves = nchunk < kStatWaves ? (int)nchunk : kStatWaves;
+    hipLaunchKernelGGL(k_act_stats<T>, dim3((unsigned)((in + 63) / 64)), dim3(waves * 64), 0, st, X,
+                       tokens, in, xmag);
     return hipGetLastError();
 }
 
 hipError_t launch_act_stats(const void *X, int dtype, int64_t tokens, int64_t in, float *xmag,
-                            double *partial, hipStream_t st)
+                            hipStream_t st)
 {
-    // Vector width: whole 8-byte loads when the row length keeps them aligned.
     switch (dtype) {
-    case AWQ_F32:
-        return in % 2 == 0 ? stats_typed<float, 2>((const float *)X, tokens, in, xmag, partial, st)
-                           : stats_typed<float, 1>((const float *)X, tokens, in, xmag, partial, st);
-    case AWQ_F16:
-        return in % 4 == 0 ? stats_typed<f16, 4>((const f16 *)X, tokens, in, xmag, partial, st)
-                           : stats_typed<f16, 1>((const f16 *)X, tokens, in, xmag, partial, st);
-    default:
-        return in % 4 == 0 ? stats_typed<bf16, 4>((const bf16 *)X, tokens, in, xmag, partial, st)
-                           : stats_typed<bf16, 1>((const bf16 *)X, tokens, in, xmag, partial, st);
+    case AWQ_F32: return stats_typed<float>((const float *)X, tokens, in, xmag, st);
+    case AWQ_F16: return stats_typed<f16>((const f16 *)X, tokens, in, xmag, st);
+    default: return stats_typed<bf16>((const bf16 *)X, tokens, in, xmag, st);
     }
 }
 
-// One block per candidate k: fp64 powers, block-wide max and min (exact, so
-// the reduction order does not matter), centring, one rounding to fp32. The
-// powers are recomputed in the second pass rather than stored. unit[k] is set
-// when all powers are equal (k = 0, or flat activations): then every s is
-// exactly 1 (sqrt(p*p) == p in binary floating point) and the search treats
-// the candidate's scaled weights as the raw stored values.
-__global__ __launch_bounds__(1024) void k_s_table(const float *__restrict__ xmag, int64_t in,
-                                                   int grid, float *__restrict__ s_tab,
-                                                   float *__restrict__ inv_tab,
-                                                   int32_t *__restrict__ unit)
+// One block per (256 columns, candidate k). For alpha >= 0, x -> x^alpha is
+// non-decreasing, and the fp32 inputs are at least one fp32 ulp (2^-23
+// relative) apart, far more than any error of an fp64 pow, so
+//   max_j pow(x_j, alpha) == pow(max_j x_j, alpha)   (and likewise for min)
+// holds for the computed values too: every block finds max and min of xmag
+// itself (exact, any order) and powers only those two and its own columns.
+// unit[k] is set when the two powers are equal (k = 0, or flat activations):
+// then every s is exactly 1 (sqrt(p * p) == p in binary floating point) and
+// the search treats the candidate's scaled weights as the raw stored values.
+__global__ __launch_bounds__(256) void k_s_table(const float *__restrict__ xmag, int64_t in, int grid,
+                                                  float *__restrict__ s_tab,
+                                                  float *__restrict__ inv_tab,
+                                                  int32_t *__restrict__ unit)
 {
-    __shared__ double smax[1024 / 64], smin[1024 / 64];
-    const int k = blockIdx.x;
+    __shared__ float smax[4], smin[4];
+    __shared__ double ext[2];
+    const int k = blockIdx.y;
     const double alpha = (double)k / (double)grid;
-    double lmax = -INFINITY, lmin = INFINITY;
-    for (int64_t j = threadIdx.x; j < in; j += blockDim.x) {
-        const double p = pow((double)xmag[j], alpha);
-        lmax = p > lmax ? p : lmax;
-        lmin = p < lmin ? p : lmin;
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool col_ok = j < in;
+    const double p = pow((double)xmag[col_ok ? j : 0], alpha);
+
+    float lmax = 0.f, lmin = FLT_MAX;   // xmag > 0
+    for (int64_t i = threadIdx.x; i < in; i += 256) {
+        const float x = xmag[i];
+        lmax = fmaxf(lmax, x);
+        lmin = fminf(lmin, x);
     }
     for (int off = 32; off > 0; off >>= 1) {
-        const double a = __shfl_xor(lmax, off);
-        const double b = __shfl_xor(lmin, off);
-        lmax = a > lmax ? a : lmax;
-        lmin = b < lmin ? b : lmin;
+        lmax = fmaxf(lmax, __shfl_xor(lmax, off));
+        lmin = fminf(lmin, __shfl_xor(lmin, off));
     }
-    const int wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
     if ((threadIdx.x & 63) == 0) {
-        smax[wave] = lmax;
-        smin[wave] = lmin;
+        smax[threadIdx.x >> 6] = lmax;
+        smin[threadIdx.x >> 6] = lmin;
     }
     __syncthreads();
-    double pmax = smax[0], pmin = smin[0];
-    for (int w = 1; w < nw; ++w) {
-        pmax = smax[w] > pmax ? smax[w] : pmax;
-        pmin = smin[w] < pmin ? smin[w] : pmin;
+    if (threadIdx.x < 2) {
+        const float xm = threadIdx.x == 0 ? fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]))
+                                          : fminf(fminf(smin[0], smin[1]), fminf(smin[2], smin[3]));
+        ext[threadIdx.x] = pow((double)xm, alpha);
     }
-    const double centre = sqrt(pmax * pmin);
-    if (unit && threadIdx.x == 0)
+    __syncthreads();
+    const double pmax = ext[0], pmin = ext[1];
+    if (unit && blockIdx.x == 0 && threadIdx.x == 0)
         unit[k] = pmax == pmin ? 1 : 0;
-    for (int64_t j = threadIdx.x; j < in; j += blockDim.x) {
-        const double p = pow((double)xmag[j], alpha);
-        const float s = (float)(p / centre);
-        s_tab[(int64_t)k * in + j] = s;
-        if (inv_tab)
-            inv_tab[(int64_t)k * in + j] = 1.0f / s;
-    }
+    if (!col_ok)
+        return;
+    const float s = (float)(p / sqrt(pmax * pmin));
+    s_tab[(int64_t)k * in + j] = s;
+    if (inv_tab)
+        inv_tab[(int64_t)k * in + j] = 1.0f / s;
 }
 
 hipError_t launch_s_table(const float *xmag, int64_t in, int grid, float *s_tab, float *inv_tab,
                           int32_t *unit, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_s_table, dim3((unsigned)(grid + 1)), dim3(1024), 0, st, xmag, in, grid,
-                       s_tab, inv_tab, unit);
+    hipLaunchKernelGGL(k_s_table, dim3((unsigned)((in + 255) / 256), (unsigned)(grid + 1)), dim3(256),
+                       0, st, xmag, in, grid, s_tab, inv_tab, unit);
     return hipGetLastError();
 }
 
