@@ -257,8 +257,30 @@ __device__ __forceinline__ void build_tile(const float (&v)[KS][8], float levels
     }
 }
 
+// Logical block coordinates (row block, token block, candidate pass).
+// Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
+// own L2. When the row blocks split evenly over the XCDs, the blocks that
+// share W rows (every token block and candidate pass of one row block) get
+// consecutive places in one XCD's dispatch order, so those rows come from
+// HBM once and then from that XCD's L2; otherwise the grid is used as is.
+constexpr int kXcds = 8;
+struct BlockCoord {
+    int64_t x, y, z;
+};
+__device__ __forceinline__ BlockCoord block_coord()
+{
+    const int64_t nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
+    if (nx % kXcds != 0)
+        return {(int64_t)blockIdx.x, (int64_t)blockIdx.y, (int64_t)blockIdx.z};
+    const int64_t lin = blockIdx.x + nx * (blockIdx.y + ny * (int64_t)blockIdx.z);
+    const int64_t xcd = lin % kXcds, k = lin / kXcds;
+    const int64_t per = ny * nz;   // blocks per row block: passes fastest, then token blocks
+    const int64_t rem = k % per;
+    return {(k / per) * kXcds + xcd, rem / nz, rem % nz};
+}
+
 // One block: 16 output rows x 256 tokens x NA candidates (candidates a0 ..
-// a0 + NA - 1, a0 = NA * blockIdx.z), 8 waves of 32 tokens, two per SIMD.
+// a0 + NA - 1, a0 = NA * pass), 8 waves of 32 tokens, two per SIMD.
 //
 // Software pipeline over groups of G input columns, one barrier per group:
 // the D tiles live in two LDS buffers selected by group parity. In the
@@ -296,14 +318,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     const int wave = threadIdx.x >> 6;
     const int r = lane & 15;           // row inside the tile (B operand column n)
     const int c = lane >> 4;           // which 8-column slice of a 32-column step
-    const int64_t row = (int64_t)blockIdx.x * 16 + r;
+    const BlockCoord bc = block_coord();
+    const int64_t row = bc.x * 16 + r;
     const bool row_ok = row < out;
     const int64_t row_c = row_ok ? row : out - 1;
-    const int64_t tok0 = (int64_t)blockIdx.y * kTokPerBlock + wave * kTokPerWave;
-    const int a0 = blockIdx.z * NA;
+    const int64_t tok0 = bc.y * kTokPerBlock + wave * kTokPerWave;
+    const int a0 = (int)bc.z * NA;
     const int na = n_alpha - a0 < NA ? n_alpha - a0 : NA;
     const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
-    const int64_t blk = (int64_t)blockIdx.x * gridDim.y + blockIdx.y;
+    const int64_t blk = bc.x * gridDim.y + bc.y;
 
     const float levels = (float)((1 << (bits - 1)) - 1);
     const float maxq = (float)((1 << bits) - 1);
