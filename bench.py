@@ -25,7 +25,7 @@ PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 METRIC = "AWQ search: α-candidate·MACs/s + ms per layer (4096×4096, 256 tok, g128, 21 α)"
 SEARCH_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_search.hip")
-PMC_FILE = os.path.join(ROOT, "profiles", "k_search_linear4096_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "k_search_linear_4096x4096_t256_hbm_counters.json")
 
 
 def parse():
