@@ -48,14 +48,14 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(alg_launch):
+def traffic_from_profile(config):
     """HBM bytes per search launch from committed rocprofv3 counters, or None
-    when none are committed for the current kernel source."""
+    when none are committed for this workload and the current kernel source."""
     if not os.path.exists(PMC_FILE):
         return None
     with open(PMC_FILE) as f:
         d = json.load(f)
-    if d.get("k_search_source_sha256_16") != source_hash(SEARCH_SRC):
+    if d.get("config") != config or d.get("k_search_source_sha256_16") != source_hash(SEARCH_SRC):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -182,7 +182,7 @@ def main():
                    "input_dtype": spec.dtype, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "k_search", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic_from_profile(search_flops)},
+                     "traffic": traffic_from_profile(spec.name)},
         "stages_ms": avg,
         "search_alpha_macs_per_s": alpha_macs / (avg["search"] * 1e-3),
         "stats_gbs": stats_bytes / (avg["stats"] * 1e-3) / 1e9,
