@@ -7,8 +7,10 @@ is the 4096x4096 fp16 linear layer with 256 calibration tokens, int4
 symmetric, group 128, grid 20 (21 alpha candidates), on seeded synthetic data.
 
 Prints one JSON line. Timing: HIP events recorded on the stream the library
-launches on (torch's current stream), around every stage of every step;
-`value` is alpha-candidate MACs per second over whole steps.
+launches on (torch's current stream). `value` is alpha-candidate MACs per
+second over K whole steps timed back to back; a second run of K steps with
+events between the stages gives the per-stage times and the search kernel's
+time for the roofline.
 """
 import argparse
 import hashlib
@@ -136,20 +138,29 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # Timed region: K whole steps back to back, one event pair around them.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # Stage breakdown (and the search kernel's time for the roofline): the
+    # same K steps again with events between the stages.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for k in range(args.steps):
         step(events[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
     per = {s: [] for s in stages}
     for ev in events:
         for i, s in enumerate(stages):
             per[s].append(ev[i].elapsed_time(ev[i + 1]))
-    gpu_total_ms = events[0][0].elapsed_time(events[-1][5])
-    ms_per_step = gpu_total_ms / args.steps
     avg = {s: sum(v) / len(v) for s, v in per.items()}
 
     alpha_macs = spec.alpha_macs

@@ -108,6 +108,9 @@ SEARCH_CASES = [
     (2, 1, 32, 1, dict(group=32, grid=1)),                         # smallest shape (fp32 operands)
     (3, 72, 512, 300, {}),                                         # few rows (fp32 operands)
     (1, 300, 256, 8, {}),                                          # few tokens (fp32 operands)
+    (2, 256, 256, 33, dict(group=32, bits=8, mode="sym")),         # bf16, 8-bit, g32
+    (1, 256, 512, 48, dict(group=64, bits=6, mode="asym")),        # f16, 6-bit asym, g64
+    (3, 264, 384, 256, dict(group=128, bits=7, mode="sym")),       # bf16, 7-bit, ragged rows
 ]
 
 
