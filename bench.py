@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -27,6 +28,7 @@ PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 METRIC = "AWQ search: α-candidate·MACs/s + ms per layer (4096×4096, 256 tok, g128, 21 α)"
 SEARCH_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_search.hip")
+MFMA_PROBE = os.path.join(ROOT, "post_weight_quantization_30_amd", "mfma_peak")
 PMC_FILE = os.path.join(ROOT, "profiles", "k_search_linear_4096x4096_t256_hbm_counters.json")
 
 
@@ -42,6 +44,8 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run a plain device copy of known size (HBM counter calibration)")
+    p.add_argument("--no-mfma-peak", action="store_true",
+                   help="skip the attainable-MFMA-peak probe")
     return p.parse_args()
 
 
@@ -60,6 +64,18 @@ def traffic_from_profile(config):
     if d.get("config") != config or d.get("k_search_source_sha256_16") != source_hash(SEARCH_SRC):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def measured_mfma_peak():
+    """Attainable dense 16x16x32 MFMA throughput from the standalone probe
+    program (a child process; None if it is not built or fails)."""
+    if not os.path.exists(MFMA_PROBE):
+        return None
+    try:
+        r = subprocess.run([MFMA_PROBE], capture_output=True, text=True, timeout=120)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
 
 
 def cpu_baseline(spec, lay, target_s):
@@ -95,6 +111,8 @@ def main():
               "single MI355X (sharding over GPUs is described in DESIGN.md, not run).",
               file=sys.stderr)
         sys.exit(2)
+
+    probe = None if args.no_mfma_peak else measured_mfma_peak()
 
     import torch
     from post_weight_quantization_30_amd import awq, synth
@@ -163,12 +181,33 @@ def main():
             per[s].append(ev[i].elapsed_time(ev[i + 1]))
     avg = {s: sum(v) / len(v) for s, v in per.items()}
 
+    # Cold-cache statistics and pack: a 512 MiB write before each launch
+    # evicts X and W from the 256 MiB Infinity Cache.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = {"stats": [], "pack": []}
+    for r in range(5):
+        for name, fn in (("stats", lambda: awq.act_stats(X, xmag, ws_s)),
+                         ("pack", lambda: awq.quantize_pack(W, s_best, spec.bits, spec.group, spec.mode,
+                                                            qweight, scales, zeros))):
+            flush.fill_(r)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            cold[name].append(e0.elapsed_time(e1))
+    del flush
+    cold_ms = {k: sorted(v)[len(v) // 2] for k, v in cold.items()}
+
     alpha_macs = spec.alpha_macs
     value = alpha_macs / (ms_per_step * 1e-3)
     search_flops = 2.0 * alpha_macs
     fp32_ops = spec.dtype == "f32" or out < 256 or T < 16
     peak = PEAK_F32_TFLOPS if fp32_ops else PEAK_F16_TFLOPS
     achieved = search_flops / (avg["search"] * 1e-3) / 1e12
+    measured = None
+    if probe and not fp32_ops:
+        measured = probe["mfma_16x16x32_f16_tflops" if spec.dtype == "f16" else "mfma_16x16x32_bf16_tflops"]
     esize = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
     stats_bytes = T * n_in * esize + 4 * n_in
     pack_bytes = out * n_in * esize + 4 * n_in + out * n_in * spec.bits / 8 + 5 * out * (n_in // spec.group)
@@ -193,11 +232,15 @@ def main():
                    "input_dtype": spec.dtype, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "k_search", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic_from_profile(spec.name)},
+                     "traffic": traffic_from_profile(spec.name),
+                     "peak_measured": measured, "frac_of_measured": achieved / measured if measured else None},
         "stages_ms": avg,
         "search_alpha_macs_per_s": alpha_macs / (avg["search"] * 1e-3),
         "stats_gbs": stats_bytes / (avg["stats"] * 1e-3) / 1e9,
         "pack_gbs": pack_bytes / (avg["pack"] * 1e-3) / 1e9,
+        "stats_gbs_cold": stats_bytes / (cold_ms["stats"] * 1e-3) / 1e9,
+        "pack_gbs_cold": pack_bytes / (cold_ms["pack"] * 1e-3) / 1e9,
+        "mfma_probe": probe,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "result": {"best_index": b, "best_alpha": b / grid if b >= 0 else None,
                    "awq_mse": float(m[b]) if b >= 0 else None, "rtn_mse": float(m[0])},

@@ -17,6 +17,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libawq.so")
 SOURCES = ["abi.hip", "k_stats.hip", "k_search.hip", "k_pack.hip"]
+# Standalone measurement program: the attainable MFMA peak (bench.py runs it).
+PROBE_SRC = "mfma_peak.hip"
+PROBE = os.path.join(PKG, "mfma_peak")
 ARCH = "gfx950"
 
 CFLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-ffp-contract=off",
@@ -57,6 +60,13 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    cmd = [_hipcc(), *[f for f in CFLAGS if f != "-fPIC"], os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
