@@ -136,6 +136,8 @@ int awq_search_finish(int64_t out, int64_t in, int64_t tokens, int grid, double 
  *     zero = rne(-lo / scale), code = clamp(rne(v / scale) + zero, 0, maxq).
  * All in fp32 with IEEE division and round-half-to-even, in exactly this order:
  * the outputs are bit-exact. Dequantize as scale * (code - zero).
+ * Non-finite W or s: the scales, zeros and codes of the groups they touch are
+ * unspecified (no error is reported); all other groups are unaffected.
  *   W:       device (out, in) of `dtype`;  s: device fp32[in] (e.g. s_best).
  *   qweight: device uint32[out][in * bits / 32 rounded up] (output): code i of a
  *            row at bits [i*bits, (i+1)*bits) of the row's little-endian stream

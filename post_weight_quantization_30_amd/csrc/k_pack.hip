@@ -24,6 +24,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace awq {
 
 template <int BITS>
@@ -46,6 +48,22 @@ __device__ __forceinline__ void pack_store(const uint32_t (&code)[32], uint32_t 
         dst[k] = word[k];
 }
 
+// fp32(w * s) for the low (H = 0) or high (H = 1) fp16 of a packed pair in
+// one v_fma_mix_f32: the fp16 source is widened exactly and w * s + (-0) is
+// rounded once, which is the product itself, signed zeros included.
+template <int H>
+__device__ __forceinline__ float mul_f16_exact(uint32_t pair, float s)
+{
+    float r;
+    const float nz = -0.0f;
+    if (H == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(s), "v"(nz));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r)
+            : "v"(pair), "v"(s), "v"(nz));
+    return r;
+}
+
 // a / b rounded to nearest even, for finite b >= 1e-8 and y = a correctly
 // rounded 1/b (an IEEE division, once per group). q0 = a*y is within 2 ulp of
 // a/b; one residual step (the residual a - b*q is exact or nearly so in an
@@ -63,7 +81,12 @@ __device__ __forceinline__ float div_rn(float a, float b, float y)
 // codes of one lane's 32 values: clamp(rne(v / scale) + zero, lo, hi) for
 // asymmetric, clamp(rne(v / scale), lo, hi) + zero for symmetric. FAST uses
 // div_rn (finite scale), otherwise the IEEE division (infinite scale, where
-// the residual steps would turn 0 * inf into NaN).
+// the residual steps would turn 0 * inf into NaN). With a finite scale and
+// finite values only the asymmetric upper bound can bind: |v| / scale <=
+// L (1 + 2^-23) < L + 1/2 for symmetric groups, and rne(v / scale) >=
+// rne(lo / scale) = -zero for asymmetric ones (rne is odd and monotone), so
+// FAST drops the other clamps. (Codes of groups with NaN values are
+// unspecified.)
 template <bool ASYM, bool FAST>
 __device__ __forceinline__ void codes(const float (&v)[32], float scale, float lo, float hi, float zero,
                                       uint32_t (&code)[32])
@@ -74,10 +97,11 @@ __device__ __forceinline__ void codes(const float (&v)[32], float scale, float l
         const float u = FAST ? div_rn(v[i], scale, y) : v[i] / scale;
         float q = rintf(u);
         if (ASYM) {
-            q = fminf(fmaxf(q + zero, lo), hi);
+            q = FAST ? fminf(q + zero, hi) : fminf(fmaxf(q + zero, lo), hi);
             code[i] = (uint32_t)(int)q;
         } else {
-            q = fminf(fmaxf(q, lo), hi);
+            if (!FAST)
+                q = fminf(fmaxf(q, lo), hi);
             code[i] = (uint32_t)((int)q + (int)zero);
         }
     }
@@ -103,12 +127,22 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
         const float *sp = s + ch * 32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            float w8[8];
-            widen8<T>(load8(wp + q * 8), w8);
             const f32x8 s8 = *reinterpret_cast<const f32x8 *>(sp + q * 8);
+            if constexpr (std::is_same<T, f16>::value) {
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 pr = __builtin_bit_cast(u32x4, load8(wp + q * 8));
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[q * 8 + i] = w8[i] * s8[i];
+                for (int e = 0; e < 4; ++e) {
+                    v[q * 8 + 2 * e] = mul_f16_exact<0>(pr[e], s8[2 * e]);
+                    v[q * 8 + 2 * e + 1] = mul_f16_exact<1>(pr[e], s8[2 * e + 1]);
+                }
+            } else {
+                float w8[8];
+                widen8<T>(load8(wp + q * 8), w8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    v[q * 8 + i] = w8[i] * s8[i];
+            }
         }
     } else {
 #pragma unroll
@@ -122,8 +156,8 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
         const float levels = (float)((1 << (bits - 1)) - 1);
         float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-            m = fmaxf(m, fabsf(v[i]));
+        for (int i = 0; i < 32; i += 2)
+            m = fmaxf(fmaxf(m, fabsf(v[i])), fabsf(v[i + 1]));
         for (int off = 1; off < lanes_per_group; off <<= 1)
             m = fmaxf(m, __shfl_xor(m, off));
         scale = fmaxf(m / levels, 1e-8f);

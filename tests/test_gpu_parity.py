@@ -222,26 +222,60 @@ def test_quantize_pack_bitwise(awq, ref, dt, mode, bits, group):
     assert np.array_equal(z.cpu().numpy(), z_o)
 
 
-def test_quantize_pack_edge_values(awq, ref):
-    """All-zero groups (scale floor), exact ties, same-sign groups, huge and tiny values."""
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_quantize_pack_edge_values(awq, ref, dt):
+    """All-zero groups (scale floor), exact ties, same-sign groups, signed
+    zeros, huge and tiny values; fp16 weights take the fused widen-and-scale
+    path."""
     n_in = 256
-    W = np.zeros((6, n_in), np.float32)
+    big, small = (1e30, 1e-30) if dt == "f32" else (6e4, 1e-7)
+    W = np.zeros((7, n_in), np.float32)
     W[1, :128] = np.linspace(-7, 7, 128) * 0.5           # many exact half-way points
     W[2, :] = np.abs(np.random.default_rng(0).standard_normal(n_in)) + 0.1
     W[3, :] = -W[2, :]
-    W[4, :] = np.random.default_rng(1).standard_normal(n_in) * 1e-30
-    W[5, :] = np.random.default_rng(2).standard_normal(n_in) * 1e30
+    W[4, :] = np.random.default_rng(1).standard_normal(n_in) * small
+    W[5, :] = np.random.default_rng(2).standard_normal(n_in) * big / 4
+    W[6, ::2] = -0.0
+    if dt == "f16":
+        W = W.astype(np.float16).astype(np.float32)
     s = np.ones(n_in, np.float32)
-    say("pack edge values")
+    s[200:] = 0.75
+    say("pack edge values", dt)
+    Wd = torch.from_numpy(W).cuda()
+    if dt == "f16":
+        Wd = Wd.half()
     for mode in ("sym", "asym"):
         for bits in (2, 3, 4):
-            q, sc, z = awq.quantize_pack(torch.from_numpy(W).cuda(), torch.from_numpy(s).cuda(),
-                                         bits, 32, mode)
+            q, sc, z = awq.quantize_pack(Wd, torch.from_numpy(s).cuda(), bits, 32, mode)
             torch.cuda.synchronize()
             q_o, sc_o, z_o = ref.quantize_pack(W, s, bits, 32, mode)
             assert np.array_equal(q.cpu().numpy().view(np.uint32), q_o), (mode, bits)
             assert np.array_equal(sc.cpu().numpy(), sc_o), (mode, bits)
             assert np.array_equal(z.cpu().numpy(), z_o), (mode, bits)
+
+
+def test_quantize_pack_nonfinite_groups_stay_local(awq, ref):
+    """Groups holding NaN or inf get unspecified codes; every other group of
+    the same call is still exact."""
+    n_in, g, bits = 256, 32, 4
+    W = np.random.default_rng(3).standard_normal((4, n_in)).astype(np.float32) * 0.02
+    W[0, 5] = np.nan
+    W[1, 40] = np.inf
+    W[2, 100] = -np.inf
+    s = np.ones(n_in, np.float32)
+    bad = np.zeros((4, n_in // g), bool)
+    bad[0, 0] = bad[1, 1] = bad[2, 3] = True
+    say("pack non-finite groups")
+    for mode in ("sym", "asym"):
+        q, sc, z = awq.quantize_pack(torch.from_numpy(W).cuda(), torch.from_numpy(s).cuda(), bits, g, mode)
+        torch.cuda.synchronize()
+        ok = ~bad
+        Wc = np.where(np.isfinite(W), W, 0.0).astype(np.float32)   # oracle only on finite groups
+        q_o, sc_o, z_o = ref.quantize_pack(Wc, s, bits, g, mode)
+        words = q.cpu().numpy().view(np.uint32).reshape(4, n_in // g, bits)
+        assert np.array_equal(words[ok], q_o.reshape(4, n_in // g, bits)[ok]), mode
+        assert np.array_equal(sc.cpu().numpy()[ok], sc_o[ok]), mode
+        assert np.array_equal(z.cpu().numpy()[ok], z_o[ok]), mode
 
 
 # ---------------------------------------------------------------------------
