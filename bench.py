@@ -36,7 +36,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="linear_4096x4096_t256",
                    help="workload name (one of synth.CONFIGS)")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -28,26 +28,6 @@
 
 namespace awq {
 
-template <int BITS>
-__device__ __forceinline__ void pack_store(const uint32_t (&code)[32], uint32_t *dst)
-{
-    uint32_t word[BITS];
-#pragma unroll
-    for (int k = 0; k < BITS; ++k)
-        word[k] = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int bit = i * BITS;
-        const int wi = bit >> 5, sh = bit & 31;
-        word[wi] |= code[i] << sh;
-        if (sh + BITS > 32)
-            word[wi + 1] |= code[i] >> (32 - sh);
-    }
-#pragma unroll
-    for (int k = 0; k < BITS; ++k)
-        dst[k] = word[k];
-}
-
 // fp32(w * s) for the low (H = 0) or high (H = 1) fp16 of a packed pair in
 // one v_fma_mix_f32: the fp16 source is widened exactly and w * s + (-0) is
 // rounded once, which is the product itself, signed zeros included.
@@ -87,30 +67,39 @@ __device__ __forceinline__ float div_rn(float a, float b, float y)
 // rne(lo / scale) = -zero for asymmetric ones (rne is odd and monotone), so
 // FAST drops the other clamps. (Codes of groups with NaN values are
 // unspecified.)
-template <bool ASYM, bool FAST>
+template <int BITS, bool ASYM, bool FAST>
 __device__ __forceinline__ void codes(const float (&v)[32], float scale, float lo, float hi, float zero,
-                                      uint32_t (&code)[32])
+                                      uint32_t (&word)[BITS])
 {
     const float y = FAST ? 1.0f / scale : 0.0f;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k)
+        word[k] = 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const float u = FAST ? div_rn(v[i], scale, y) : v[i] / scale;
         float q = rintf(u);
+        uint32_t code;
         if (ASYM) {
             q = FAST ? fminf(q + zero, hi) : fminf(fmaxf(q + zero, lo), hi);
-            code[i] = (uint32_t)(int)q;
+            code = (uint32_t)(int)q;
         } else {
             if (!FAST)
                 q = fminf(fmaxf(q, lo), hi);
-            code[i] = (uint32_t)((int)q + (int)zero);
+            code = (uint32_t)((int)q + (int)zero);
         }
+        // code i at bits [i*BITS, (i+1)*BITS) of the lane's BITS words
+        const int bit = i * BITS, wi = bit >> 5, sh = bit & 31;
+        word[wi] |= code << sh;
+        if (sh + BITS > 32)
+            word[wi + 1] |= code >> (32 - sh);
     }
 }
 
-template <typename T>
+template <typename T, int BITS>
 __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, int64_t out,
                                                         int64_t in, const float *__restrict__ s,
-                                                        int bits, int lanes_per_group, int mode,
+                                                        int lanes_per_group, int mode,
                                                         uint32_t *__restrict__ qweight,
                                                         float *__restrict__ scales,
                                                         uint8_t *__restrict__ zeros)
@@ -150,10 +139,10 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
             v[i] = 0.f;
     }
 
-    uint32_t code[32];
+    uint32_t word[BITS];
     float scale, zero;
     if (mode == AWQ_SYM) {
-        const float levels = (float)((1 << (bits - 1)) - 1);
+        const float levels = (float)((1 << (BITS - 1)) - 1);
         float m = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; i += 2)
@@ -161,13 +150,13 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
         for (int off = 1; off < lanes_per_group; off <<= 1)
             m = fmaxf(m, __shfl_xor(m, off));
         scale = fmaxf(m / levels, 1e-8f);
-        zero = (float)(1 << (bits - 1));
+        zero = (float)(1 << (BITS - 1));
         if (scale <= FLT_MAX)
-            codes<false, true>(v, scale, -levels - 1.0f, levels, zero, code);
+            codes<BITS, false, true>(v, scale, -levels - 1.0f, levels, zero, word);
         else
-            codes<false, false>(v, scale, -levels - 1.0f, levels, zero, code);
+            codes<BITS, false, false>(v, scale, -levels - 1.0f, levels, zero, word);
     } else {
-        const float maxq = (float)((1 << bits) - 1);
+        const float maxq = (float)((1 << BITS) - 1);
         float lo = 0.f, hi = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
@@ -181,23 +170,17 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
         scale = fmaxf((hi - lo) / maxq, 1e-8f);
         zero = rintf(-lo / scale);
         if (scale <= FLT_MAX)
-            codes<true, true>(v, scale, 0.0f, maxq, zero, code);
+            codes<BITS, true, true>(v, scale, 0.0f, maxq, zero, word);
         else
-            codes<true, false>(v, scale, 0.0f, maxq, zero, code);
+            codes<BITS, true, false>(v, scale, 0.0f, maxq, zero, word);
     }
     if (!active)
         return;
 
-    uint32_t *dst = qweight + row * (chunks * bits) + ch * bits;
-    switch (bits) {
-    case 2: pack_store<2>(code, dst); break;
-    case 3: pack_store<3>(code, dst); break;
-    case 4: pack_store<4>(code, dst); break;
-    case 5: pack_store<5>(code, dst); break;
-    case 6: pack_store<6>(code, dst); break;
-    case 7: pack_store<7>(code, dst); break;
-    default: pack_store<8>(code, dst); break;
-    }
+    uint32_t *dst = qweight + row * (chunks * BITS) + ch * BITS;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k)
+        dst[k] = word[k];
     if (ch % lanes_per_group == 0) {
         const int64_t gi = row * (in / (32 * lanes_per_group)) + ch / lanes_per_group;
         scales[gi] = scale;
@@ -205,25 +188,41 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
     }
 }
 
+template <typename T>
+static void pack_typed(const T *W, int64_t out, int64_t in, const float *s, int bits, int lpg, int mode,
+                       uint32_t *qweight, float *scales, uint8_t *zeros, hipStream_t st)
+{
+    const int64_t threads = out * (in / 32);
+    dim3 grid((unsigned)((threads + 255) / 256));
+#define AWQ_PACK_LAUNCH(B)                                                                        \
+    hipLaunchKernelGGL((k_quantize_pack<T, B>), grid, dim3(256), 0, st, W, out, in, s, lpg, mode, \
+                       qweight, scales, zeros)
+    switch (bits) {
+    case 2: AWQ_PACK_LAUNCH(2); break;
+    case 3: AWQ_PACK_LAUNCH(3); break;
+    case 4: AWQ_PACK_LAUNCH(4); break;
+    case 5: AWQ_PACK_LAUNCH(5); break;
+    case 6: AWQ_PACK_LAUNCH(6); break;
+    case 7: AWQ_PACK_LAUNCH(7); break;
+    default: AWQ_PACK_LAUNCH(8); break;
+    }
+#undef AWQ_PACK_LAUNCH
+}
+
 hipError_t launch_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s, int bits,
                        int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros,
                        hipStream_t st)
 {
     const int lpg = group / 32;
-    const int64_t threads = out * (in / 32);
-    dim3 grid((unsigned)((threads + 255) / 256));
     switch (dtype) {
     case AWQ_F32:
-        hipLaunchKernelGGL(k_quantize_pack<float>, grid, dim3(256), 0, st, (const float *)W, out, in,
-                           s, bits, lpg, mode, qweight, scales, zeros);
+        pack_typed((const float *)W, out, in, s, bits, lpg, mode, qweight, scales, zeros, st);
         break;
     case AWQ_F16:
-        hipLaunchKernelGGL(k_quantize_pack<f16>, grid, dim3(256), 0, st, (const f16 *)W, out, in, s,
-                           bits, lpg, mode, qweight, scales, zeros);
+        pack_typed((const f16 *)W, out, in, s, bits, lpg, mode, qweight, scales, zeros, st);
         break;
     default:
-        hipLaunchKernelGGL(k_quantize_pack<bf16>, grid, dim3(256), 0, st, (const bf16 *)W, out, in,
-                           s, bits, lpg, mode, qweight, scales, zeros);
+        pack_typed((const bf16 *)W, out, in, s, bits, lpg, mode, qweight, scales, zeros, st);
         break;
     }
     return hipGetLastError();
