@@ -113,11 +113,21 @@ __global__ __launch_bounds__(256) void k_s_table(const float *__restrict__ xmag,
     const bool col_ok = j < in;
     const double p = pow((double)xmag[col_ok ? j : 0], alpha);
 
-    float lmax = 0.f, lmin = FLT_MAX;   // xmag > 0
-    for (int64_t i = threadIdx.x; i < in; i += 256) {
-        const float x = xmag[i];
-        lmax = fmaxf(lmax, x);
-        lmin = fminf(lmin, x);
+    // Max and min of xmag (> 0): 16 independent loads in flight per thread
+    // per round (one round for in <= 4096).
+    float lmax = 0.f, lmin = FLT_MAX;
+    for (int64_t i0 = threadIdx.x; i0 < in; i0 += 256 * 16) {
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int64_t i = i0 + 256 * u;
+            x[u] = xmag[i < in ? i : i0];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            lmax = fmaxf(lmax, x[u]);
+            lmin = fminf(lmin, x[u]);
+        }
     }
     for (int off = 32; off > 0; off >>= 1) {
         lmax = fmaxf(lmax, __shfl_xor(lmax, off));
