@@ -640,8 +640,22 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_finish(const double *__re
     }
     __syncthreads();
     const int bi = sbest;
-    for (int64_t j = threadIdx.x; j < in; j += blockDim.x)
-        s_best[j] = bi >= 0 ? s_tab[(int64_t)bi * in + j] : 1.0f;
+    const float *src = s_tab + (int64_t)(bi >= 0 ? bi : 0) * in;
+    // four independent loads in flight per thread per round
+    for (int64_t j0 = threadIdx.x; j0 < in; j0 += 4 * (int64_t)blockDim.x) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = j0 + u * (int64_t)blockDim.x;
+            x[u] = bi >= 0 && j < in ? src[j] : 1.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = j0 + u * (int64_t)blockDim.x;
+            if (j < in)
+                s_best[j] = x[u];
+        }
+    }
 }
 
 template <typename TIn, typename TOp, int G>
