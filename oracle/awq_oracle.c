@@ -338,6 +338,145 @@ done:
 }
 
 /* ---------------------------------------------------------------------------
+ * Clipping-range search. [G] "Simplifications" names a per-group clipping
+ * threshold that shrinks the max range to cut rounding error; [C] "AWQ: move
+ * the error away from what matters" describes a second search after the
+ * alpha search that shrinks each group's clipping range a little when that
+ * lowers output error, then plain RTN. The pages fix no numbers; the readings
+ * used here:
+ *   - shrink ratios r_i = fl32(1 - i * max_shrink / n_clip), i = 0..n_clip-1,
+ *     computed in fp64 and rounded once (r_0 = 1: no clipping);
+ *   - the clipping range of a group is the quantizer's own range scaled by r:
+ *     symmetric [-r*A, r*A] with A = max|v|; asymmetric [r*lo, r*hi] with
+ *     lo = min(min v, 0), hi = max(max v, 0); values are clamped into it and
+ *     the scale (and zero) are those of the clipped range;
+ *   - the error of a choice is the group's own squared output error over the
+ *     calibration tokens, sum_t (sum_{j in group} X[t,j] (wq_j - w_j))^2 with
+ *     wq = fake-quantized weight / s (fp64), groups taken one at a time;
+ *   - per (row, group) the first strict minimum over i wins (NaN never).
+ * ------------------------------------------------------------------------- */
+float awq_ref_clip_ratio(int i, int n_clip, float max_shrink)
+{
+    return (float)(1.0 - (double)i * (double)max_shrink / (double)n_clip);
+}
+
+int awq_ref_quant_group_clip(const float *v, int64_t g, int bits, int mode, float ratio,
+                             int32_t *code, float *scale_out, int32_t *zero_out, float *what)
+{
+    if (!v || g < 1 || bits < 2 || bits > 8 || (mode != AWQ_REF_SYM && mode != AWQ_REF_ASYM))
+        return REF_EINVAL;
+    if (mode == AWQ_REF_SYM) {
+        const float levels = (float)((1 << (bits - 1)) - 1);
+        const int32_t offset = 1 << (bits - 1);
+        float amax = 0.0f;
+        for (int64_t i = 0; i < g; ++i) {
+            float a = fabsf(v[i]);
+            if (a > amax) amax = a;
+        }
+        const float mx = ratio * amax;          /* clipped range [-mx, mx] */
+        float scale = mx / levels;
+        if (scale < 1e-8f) scale = 1e-8f;
+        for (int64_t i = 0; i < g; ++i) {
+            float x = v[i];
+            if (x > mx) x = mx;
+            if (x < -mx) x = -mx;
+            float q = rintf(x / scale);
+            if (q < -levels - 1.0f) q = -levels - 1.0f;
+            if (q > levels) q = levels;
+            if (code) code[i] = (int32_t)q + offset;
+            if (what) what[i] = q * scale;
+        }
+        if (scale_out) *scale_out = scale;
+        if (zero_out) *zero_out = offset;
+    } else {
+        const float maxq = (float)((1 << bits) - 1);
+        float lo = v[0], hi = v[0];
+        for (int64_t i = 1; i < g; ++i) {
+            if (v[i] < lo) lo = v[i];
+            if (v[i] > hi) hi = v[i];
+        }
+        if (lo > 0.0f) lo = 0.0f;
+        if (hi < 0.0f) hi = 0.0f;
+        lo = ratio * lo;                          /* clipped range [lo, hi] */
+        hi = ratio * hi;
+        float scale = (hi - lo) / maxq;
+        if (scale < 1e-8f) scale = 1e-8f;
+        float zero = rintf(-lo / scale);
+        for (int64_t i = 0; i < g; ++i) {
+            float x = v[i];
+            if (x > hi) x = hi;
+            if (x < lo) x = lo;
+            float q = rintf(x / scale) + zero;
+            if (q < 0.0f) q = 0.0f;
+            if (q > maxq) q = maxq;
+            if (code) code[i] = (int32_t)q;
+            if (what) what[i] = scale * (q - zero);
+        }
+        if (scale_out) *scale_out = scale;
+        if (zero_out) *zero_out = (int32_t)zero;
+    }
+    return REF_OK;
+}
+
+int awq_ref_clip_search(const float *W, const float *X, int64_t out, int64_t in, int64_t tokens,
+                        const float *s, int bits, int group, int mode, int n_clip,
+                        float max_shrink, float *clip, double *sse, int nthreads)
+{
+    if (!W || !X || !s || !clip || tokens < 1 || n_clip < 1 || !(max_shrink >= 0.0f) ||
+        max_shrink >= 1.0f || check_layer(out, in, bits, group, mode) != REF_OK)
+        return REF_EINVAL;
+    const int64_t ngroups = in / group;
+    double *x64 = to_f64(X, tokens * in);
+    if (!x64)
+        return REF_EINVAL;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads())
+    for (int64_t o = 0; o < out; ++o) {
+        float *v = (float *)malloc((size_t)group * sizeof(float));
+        float *what = (float *)malloc((size_t)group * sizeof(float));
+        double *d = (double *)malloc((size_t)group * sizeof(double));
+        if (!v || !what || !d) {
+#pragma omp atomic write
+            bad = 1;
+            free(v);
+            free(what);
+            free(d);
+            continue;
+        }
+        for (int64_t gi = 0; gi < ngroups; ++gi) {
+            const int64_t g0 = gi * group;
+            for (int64_t j = 0; j < group; ++j)
+                v[j] = W[o * in + g0 + j] * s[g0 + j];
+            int best = 0;
+            double best_e = INFINITY;
+            for (int i = 0; i < n_clip; ++i) {
+                const float r = awq_ref_clip_ratio(i, n_clip, max_shrink);
+                awq_ref_quant_group_clip(v, group, bits, mode, r, NULL, NULL, NULL, what);
+                for (int64_t j = 0; j < group; ++j)
+                    d[j] = (double)what[j] / (double)s[g0 + j] - (double)W[o * in + g0 + j];
+                double e = 0.0;
+                for (int64_t t = 0; t < tokens; ++t) {
+                    const double y = dot(x64 + t * in + g0, d, group);
+                    e += y * y;
+                }
+                if (sse)
+                    sse[(o * ngroups + gi) * n_clip + i] = e;
+                if (e < best_e) {
+                    best_e = e;
+                    best = i;
+                }
+            }
+            clip[o * ngroups + gi] = awq_ref_clip_ratio(best, n_clip, max_shrink);
+        }
+        free(v);
+        free(what);
+        free(d);
+    }
+    free(x64);
+    return bad ? REF_EINVAL : REF_OK;
+}
+
+/* ---------------------------------------------------------------------------
  * Final RTN of W diag(s) and packing. What is stored follows [C] "What lands
  * on disk" (integer codes packed into 32-bit words, one scale and one zero per
  * group and output row); the bit order and axis are this library's own: code i
@@ -347,6 +486,13 @@ done:
 int awq_ref_quantize_pack(const float *W, int64_t out, int64_t in, const float *s,
                           int bits, int group, int mode, uint32_t *qweight,
                           float *scales, uint8_t *zeros)
+{
+    return awq_ref_quantize_pack_clip(W, out, in, s, NULL, bits, group, mode, qweight, scales, zeros);
+}
+
+int awq_ref_quantize_pack_clip(const float *W, int64_t out, int64_t in, const float *s,
+                               const float *clip, int bits, int group, int mode,
+                               uint32_t *qweight, float *scales, uint8_t *zeros)
 {
     if (!W || !s || !qweight || !scales || !zeros ||
         check_layer(out, in, bits, group, mode) != REF_OK)
@@ -369,7 +515,11 @@ int awq_ref_quantize_pack(const float *W, int64_t out, int64_t in, const float *
                 v[i] = W[o * in + g0 + i] * s[g0 + i];
             float scale;
             int32_t zero;
-            awq_ref_quant_group(v, group, bits, mode, code, &scale, &zero, NULL);
+            if (clip)
+                awq_ref_quant_group_clip(v, group, bits, mode, clip[o * ngroups + gi], code, &scale,
+                                         &zero, NULL);
+            else
+                awq_ref_quant_group(v, group, bits, mode, code, &scale, &zero, NULL);
             scales[o * ngroups + gi] = scale;
             zeros[o * ngroups + gi] = (uint8_t)zero;
             for (int64_t i = 0; i < group; ++i) {

@@ -92,6 +92,28 @@ int awq_ref_quantize_pack(const float *W, int64_t out, int64_t in, const float *
                           int bits, int group, int mode, uint32_t *qweight,
                           float *scales, uint8_t *zeros);
 
+/* Clipping-range search after the alpha search ([G] "Simplifications";
+ * [C] "AWQ: move the error away from what matters": a second search shrinks
+ * each group's clipping range when that lowers output error). Readings (the
+ * pages give no numbers): ratios r_i = fl32(1 - i*max_shrink/n_clip),
+ * i = 0..n_clip-1; the group's quantizer range (sym [-A, A], asym [lo, hi]
+ * with 0 included) scaled by r, values clamped into it, scale and zero from
+ * the clipped range; error = the group's own squared output error over the
+ * tokens, sum_t (X[t, group] . (Q(v)/s - w))^2 in fp64; first strict minimum.
+ * clip: fp32[out][in/group] (output, the chosen ratio); sse: optional
+ * fp64[out][in/group][n_clip]. Returns 0 or -1. */
+float awq_ref_clip_ratio(int i, int n_clip, float max_shrink);
+int awq_ref_quant_group_clip(const float *v, int64_t g, int bits, int mode, float ratio,
+                             int32_t *code, float *scale, int32_t *zero, float *what);
+int awq_ref_clip_search(const float *W, const float *X, int64_t out, int64_t in, int64_t tokens,
+                        const float *s, int bits, int group, int mode, int n_clip,
+                        float max_shrink, float *clip, double *sse, int nthreads);
+/* awq_ref_quantize_pack with a clipping ratio per (row, group) (clip may be
+ * NULL: no clipping, identical to awq_ref_quantize_pack). */
+int awq_ref_quantize_pack_clip(const float *W, int64_t out, int64_t in, const float *s,
+                               const float *clip, int bits, int group, int mode,
+                               uint32_t *qweight, float *scales, uint8_t *zeros);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,18 @@ def _load():
     lib.awq_ref_search.restype = cint
     lib.awq_ref_quantize_pack.argtypes = [f32p, i64, i64, f32p, cint, cint, cint, u32p, f32p, u8p]
     lib.awq_ref_quantize_pack.restype = cint
+    lib.awq_ref_clip_ratio.argtypes = [cint, cint, ctypes.c_float]
+    lib.awq_ref_clip_ratio.restype = ctypes.c_float
+    lib.awq_ref_quant_group_clip.argtypes = [f32p, i64, cint, cint, ctypes.c_float, i32p,
+                                             ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32),
+                                             f32p]
+    lib.awq_ref_quant_group_clip.restype = cint
+    lib.awq_ref_clip_search.argtypes = [f32p, f32p, i64, i64, i64, f32p, cint, cint, cint, cint,
+                                        ctypes.c_float, f32p, f64p, cint]
+    lib.awq_ref_clip_search.restype = cint
+    lib.awq_ref_quantize_pack_clip.argtypes = [f32p, i64, i64, f32p, ctypes.c_void_p, cint, cint, cint,
+                                               u32p, f32p, u8p]
+    lib.awq_ref_quantize_pack_clip.restype = cint
     _lib = lib
     return lib
 
@@ -135,4 +147,51 @@ def quantize_pack(W, s, bits, group, mode):
     st = _load().awq_ref_quantize_pack(W, out, n_in, _f32(s), bits, group, _MODES[mode], q, sc, z)
     if st != 0:
         raise ValueError(f"awq_ref_quantize_pack status {st}")
+    return q, sc, z
+
+
+def clip_ratio(i, n_clip, max_shrink):
+    return np.float32(_load().awq_ref_clip_ratio(i, n_clip, max_shrink))
+
+
+def quant_group_clip(v, bits, mode, ratio):
+    """quant_group with the clipping range scaled by `ratio`."""
+    v = _f32(v)
+    g = v.shape[0]
+    code = np.empty(g, np.int32)
+    what = np.empty(g, np.float32)
+    scale = ctypes.c_float()
+    zero = ctypes.c_int32()
+    st = _load().awq_ref_quant_group_clip(v, g, bits, _MODES[mode], float(ratio), code,
+                                          ctypes.byref(scale), ctypes.byref(zero), what)
+    if st != 0:
+        raise ValueError(f"awq_ref_quant_group_clip status {st}")
+    return code, np.float32(scale.value), int(zero.value), what
+
+
+def clip_search(W, X, s, bits, group, mode, n_clip=20, max_shrink=0.5, nthreads=0):
+    """Returns (clip float32[out][in/group], sse float64[out][in/group][n_clip])."""
+    W, X = _f32(W), _f32(X)
+    out, n_in = W.shape
+    clip = np.empty((out, n_in // group), np.float32)
+    sse = np.empty((out, n_in // group, n_clip), np.float64)
+    st = _load().awq_ref_clip_search(W, X, out, n_in, X.shape[0], _f32(s), bits, group, _MODES[mode],
+                                     n_clip, max_shrink, clip, sse, nthreads)
+    if st != 0:
+        raise ValueError(f"awq_ref_clip_search status {st}")
+    return clip, sse
+
+
+def quantize_pack_clip(W, s, clip, bits, group, mode):
+    """quantize_pack with a clipping ratio per (row, group)."""
+    W = _f32(W)
+    out, n_in = W.shape
+    q = np.empty((out, words_per_row(n_in, bits)), np.uint32)
+    sc = np.empty((out, n_in // group), np.float32)
+    z = np.empty((out, n_in // group), np.uint8)
+    clip = _f32(clip)
+    st = _load().awq_ref_quantize_pack_clip(W, out, n_in, _f32(s), clip.ctypes.data_as(ctypes.c_void_p),
+                                            bits, group, _MODES[mode], q, sc, z)
+    if st != 0:
+        raise ValueError(f"awq_ref_quantize_pack_clip status {st}")
     return q, sc, z

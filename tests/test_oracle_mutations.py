@@ -37,10 +37,25 @@ MUTATIONS = [
  ("asym dequant", "if (what) what[i] = scale * (q - zero);", "if (what) what[i] = scale * q;"),
  ("sym scale floor", "if (scale < 1e-8f) scale = 1e-8f;\n        for (int64_t i = 0; i < g; ++i) {\n            float q = rintf(v[i] / scale);\n            if (q < -levels", "for (int64_t i = 0; i < g; ++i) {\n            float q = rintf(v[i] / scale);\n            if (q < -levels"),
 ]
+# Mistakes in the clipping-range search, checked against its own pins.
+CLIP_MUTATIONS = [
+ ("clip ratio i+1", "return (float)(1.0 - (double)i * (double)max_shrink / (double)n_clip);",
+  "return (float)(1.0 - (double)(i + 1) * (double)max_shrink / (double)n_clip);"),
+ ("clip err without 1/s", "d[j] = (double)what[j] / (double)s[g0 + j] - (double)W[o * in + g0 + j];",
+  "d[j] = (double)what[j] - (double)W[o * in + g0 + j];"),
+ ("clip sym range unscaled", "const float mx = ratio * amax;", "const float mx = amax;"),
+ ("clip asym only hi", "lo = ratio * lo;", ";"),
+ ("clip tie last", "if (e < best_e) {", "if (e <= best_e) {"),
+ ("clip pack ignores clip", "if (clip)\n                awq_ref_quant_group_clip(", "if (0)\n                awq_ref_quant_group_clip("),
+]
 
 
-@pytest.mark.parametrize("name,before,after", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_planted_mistake_is_caught(tmp_path, name, before, after):
+CASES = ([(n, b, a, "test_oracle_pins.py") for n, b, a in MUTATIONS] +
+         [(n, b, a, "test_oracle_clip_pins.py") for n, b, a in CLIP_MUTATIONS])
+
+
+@pytest.mark.parametrize("name,before,after,pins", CASES, ids=[m[0] for m in CASES])
+def test_planted_mistake_is_caught(tmp_path, name, before, after, pins):
     src = open(SRC).read()
     assert before in src, f"pattern for '{name}' no longer in the oracle source"
     (tmp_path / "awq_oracle.c").write_text(src.replace(before, after, 1))
@@ -50,6 +65,6 @@ def test_planted_mistake_is_caught(tmp_path, name, before, after):
                     "-o", str(lib), str(tmp_path / "awq_oracle.c"), "-lm"], check=True)
     env = dict(os.environ, AWQ_ORACLE_LIB=str(lib), OMP_NUM_THREADS="4")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        env=env, capture_output=True, text=True, cwd=ROOT, timeout=600)
     assert r.returncode != 0, f"planted mistake '{name}' passed every pin:\n{r.stdout[-500:]}"
