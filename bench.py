@@ -46,6 +46,10 @@ def parse():
                    help="also run a plain device copy of known size (HBM counter calibration)")
     p.add_argument("--no-mfma-peak", action="store_true",
                    help="skip the attainable-MFMA-peak probe")
+    p.add_argument("--no-clip", action="store_true",
+                   help="skip the clipping-range search measurement")
+    p.add_argument("--clip-steps", type=int, default=10,
+                   help="timed launches of the clipping-range search")
     return p.parse_args()
 
 
@@ -102,6 +106,58 @@ def cpu_baseline(spec, lay, target_s):
     return {"value": macs / dt, "unit": "alpha-candidate MAC/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {spec.out} rows, all {spec.tokens} tokens and {spec.inn} columns, "
                       f"{spec.n_alpha} candidates; stats + search + pack; {dt:.2f} s"}
+
+
+N_CLIP, MAX_SHRINK = 20, 0.5
+
+
+def clip_measure(awq, torch, spec, W, X, s_best, args):
+    """The clipping-range search on W diag(s_best) (the step after the alpha
+    search) and the clipped pack: kernel times from HIP events on the launch
+    stream, and the fp32 MFMA roofline of the search kernel."""
+    out, n_in, T = spec.out, spec.inn, spec.tokens
+    dev = W.device
+    clip = torch.empty((out, n_in // spec.group), dtype=torch.float32, device=dev)
+    sse = torch.empty((out, n_in // spec.group, N_CLIP), dtype=torch.float64, device=dev)
+    qw = torch.empty((out, awq.words_per_row(n_in, spec.bits)), dtype=torch.int32, device=dev)
+    sc = torch.empty((out, n_in // spec.group), dtype=torch.float32, device=dev)
+    zr = torch.empty((out, n_in // spec.group), dtype=torch.uint8, device=dev)
+
+    def search():
+        awq.clip_search(W, X, s_best, spec.bits, spec.group, spec.mode, N_CLIP, MAX_SHRINK, clip=clip)
+
+    def pack():
+        awq.quantize_pack(W, s_best, spec.bits, spec.group, spec.mode, qw, sc, zr, clip=clip)
+
+    def timed(fn, k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    for _ in range(2):
+        search()
+        pack()
+    torch.cuda.synchronize()
+    ms = timed(search, args.clip_steps)
+    pack_ms = timed(pack, args.clip_steps)
+    # the chosen ratios and their errors, for the record (untimed)
+    awq.clip_search(W, X, s_best, spec.bits, spec.group, spec.mode, N_CLIP, MAX_SHRINK, clip=clip, sse=sse)
+    torch.cuda.synchronize()
+    e = sse.cpu()
+    e_best = e.min(dim=-1).values
+    macs = N_CLIP * T * out * n_in
+    achieved = 2.0 * macs / (ms * 1e-3) / 1e12
+    return {"n_clip": N_CLIP, "max_shrink": MAX_SHRINK, "ms": ms, "pack_ms": pack_ms,
+            "ratio_macs_per_s": macs / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "kernel": "k_clip_search", "achieved": achieved,
+                         "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS,
+                         "traffic": None},
+            "clipped_group_frac": float((clip < 1).float().mean().item()),
+            "group_sse_vs_unclipped": float(e_best.sum() / e[..., 0].sum())}
 
 
 def main():
@@ -245,6 +301,8 @@ def main():
         "result": {"best_index": b, "best_alpha": b / grid if b >= 0 else None,
                    "awq_mse": float(m[b]) if b >= 0 else None, "rtn_mse": float(m[0])},
     }
+    if not args.no_clip:
+        rec["clip_search"] = clip_measure(awq, torch, spec, W, X, s_best, args)
     if args.copy_calib:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -149,6 +149,55 @@ int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const f
                       int bits, int group, int mode, uint32_t *qweight, float *scales,
                       uint8_t *zeros, void *stream);
 
+/* Largest n_clip accepted by awq_clip_search. */
+#define AWQ_MAX_CLIP 64
+
+/* Clipping-range search, run after the alpha search on W diag(s_best)
+ * ("AWQ (activation-aware weight quantization)", "Simplifications": a
+ * per-group clipping threshold that shrinks the range to cut rounding error;
+ * "AWQ vs GPTQ Quantization Architectures Compared", "AWQ: move the error away
+ * from what matters": a second, smaller search after the scale search that
+ * shrinks each group's clipping range when that lowers the output error). The
+ * pages fix no numbers; this library's reading: for ratio
+ *   r_i = fp32(1 - i * max_shrink / n_clip)   (fp64 arithmetic), i = 0..n_clip-1,
+ * each group's quantizer range (see awq_quantize_pack) is scaled by r_i --
+ * symmetric [-r A, r A] with A = max|v|, asymmetric [r lo, r hi] -- the scaled
+ * weights v = fp32(W[o, j] s[j]) are clamped into it and quantized with that
+ * range's scale (and zero), Wq = dequantized value / s, and
+ *   sse[o][g][i] = sum over tokens t of ( sum_{j in group g} X[t, j] (Wq[o, j] - W[o, j]) )^2
+ * is the group's own squared output error. clip[o][g] = r_i of the first i
+ * whose sse is strictly below every earlier one (r_0 = 1, no clipping, wins
+ * ties; a NaN never wins).
+ *   W, X:       device, (out, in) and (tokens, in) of `dtype`.
+ *   s:          device fp32[in], positive (e.g. s_best of awq_search).
+ *   bits, group, mode: as for awq_quantize_pack; group in {32, 64, 128}.
+ *   n_clip:     1..AWQ_MAX_CLIP;  max_shrink: in [0, 1) (defaults in the
+ *               Python binding: 20 and 0.5).
+ *   clip:       device fp32[out][in / group] (output): the chosen ratios.
+ *   sse:        device fp64[out][in / group][n_clip] (output), or NULL.
+ * The kernel forms Wq - W from the same fp32 quantizer as awq_quantize_pack,
+ * multiplies it with X in fp32 MFMA operations (fp32 accumulation over a
+ * group) and sums the squares over tokens in fp64 in a fixed order:
+ * bitwise reproducible, each sse within a few group-length multiples of fp32
+ * rounding of the exact value; where two ratios' errors lie that close the
+ * choice between them may differ from an exact evaluation.
+ * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128}, or more than 65535 groups. */
+int awq_clip_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                    int64_t tokens, const float *s, int bits, int group, int mode, int n_clip,
+                    float max_shrink, float *clip, double *sse, void *stream);
+
+/* awq_quantize_pack with one clipping ratio per output row and group:
+ *   clip: device fp32[out][in / group], each in (0, 1] (as written by
+ *         awq_clip_search). Before quantization the group's range is scaled
+ *         by its ratio (symmetric [-r max|v|, r max|v|], asymmetric [r lo, r hi]),
+ *         v is clamped into that range, and scale and zero are those of the
+ *         scaled range, in fp32 in that order: bit-exact. A ratio of 1 gives
+ *         exactly awq_quantize_pack's outputs.
+ * All other arguments and errors as awq_quantize_pack. */
+int awq_quantize_pack_clip(const void *W, int dtype, int64_t out, int64_t in, const float *s,
+                           const float *clip, int bits, int group, int mode, uint32_t *qweight,
+                           float *scales, uint8_t *zeros, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *awq_status_string(int status);
 

@@ -16,6 +16,7 @@ F32, F16, BF16 = 0, 1, 2
 SYM, ASYM = 0, 1
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP, ERR_NONFINITE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 MAX_GRID = 1024
+MAX_CLIP = 64
 
 _DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _MODE = {"sym": SYM, "asym": ASYM, SYM: SYM, ASYM: ASYM}
@@ -60,6 +61,12 @@ def lib():
         L.awq_search_workspace_size.restype = sz
         L.awq_quantize_pack.argtypes = [vp, cint, i64, i64, vp, cint, cint, cint, vp, vp, vp, vp]
         L.awq_quantize_pack.restype = cint
+        L.awq_clip_search.argtypes = [vp, vp, cint, i64, i64, i64, vp, cint, cint, cint, cint,
+                                      ctypes.c_float, vp, vp, vp]
+        L.awq_clip_search.restype = cint
+        L.awq_quantize_pack_clip.argtypes = [vp, cint, i64, i64, vp, vp, cint, cint, cint, vp, vp,
+                                             vp, vp]
+        L.awq_quantize_pack_clip.restype = cint
         L.awq_status_string.argtypes = [cint]
         L.awq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -176,9 +183,30 @@ def search_finish(out, n_in, tokens, grid, mse, best, s_best, workspace):
         workspace.numel() * workspace.element_size(), _stream()))
 
 
-def quantize_pack(W, s, bits, group, mode, qweight=None, scales=None, zeros=None):
+def clip_search(W, X, s, bits, group, mode, n_clip=20, max_shrink=0.5, clip=None, sse=None,
+                want_sse=False):
+    """Clipping-range search on W diag(s). Returns (clip fp32 [out][in/group],
+    sse fp64 [out][in/group][n_clip] or None)."""
+    out, n_in = W.shape
+    T = X.shape[0]
+    if X.shape[1] != n_in or X.dtype != W.dtype:
+        raise ValueError("W (out, in) and X (tokens, in) must share in and dtype")
+    dev = W.device
+    if clip is None:
+        clip = torch.empty((out, n_in // group), dtype=torch.float32, device=dev)
+    if sse is None and want_sse:
+        sse = torch.empty((out, n_in // group, n_clip), dtype=torch.float64, device=dev)
+    _check("awq_clip_search", lib().awq_clip_search(
+        _dev(W, "W"), _dev(X, "X"), _dtype_code(W), out, n_in, T, _dev(s, "s", torch.float32),
+        bits, group, _MODE[mode], n_clip, float(max_shrink), _dev(clip, "clip", torch.float32),
+        None if sse is None else _dev(sse, "sse", torch.float64), _stream()))
+    return clip, sse
+
+
+def quantize_pack(W, s, bits, group, mode, qweight=None, scales=None, zeros=None, clip=None):
     """Returns device tensors (qweight int32 view of uint32 words [out][words],
-    scales fp32 [out][in/group], zeros uint8 [out][in/group])."""
+    scales fp32 [out][in/group], zeros uint8 [out][in/group]). With `clip`
+    (fp32 [out][in/group] ratios) each group's range is clipped first."""
     out, n_in = W.shape
     dev = W.device
     if qweight is None:
@@ -187,20 +215,30 @@ def quantize_pack(W, s, bits, group, mode, qweight=None, scales=None, zeros=None
         scales = torch.empty((out, n_in // group), dtype=torch.float32, device=dev)
     if zeros is None:
         zeros = torch.empty((out, n_in // group), dtype=torch.uint8, device=dev)
-    _check("awq_quantize_pack", lib().awq_quantize_pack(
-        _dev(W, "W"), _dtype_code(W), out, n_in, _dev(s, "s", torch.float32), bits, group,
-        _MODE[mode], _dev(qweight, "qweight"), _dev(scales, "scales", torch.float32),
-        _dev(zeros, "zeros", torch.uint8), _stream()))
+    if clip is None:
+        _check("awq_quantize_pack", lib().awq_quantize_pack(
+            _dev(W, "W"), _dtype_code(W), out, n_in, _dev(s, "s", torch.float32), bits, group,
+            _MODE[mode], _dev(qweight, "qweight"), _dev(scales, "scales", torch.float32),
+            _dev(zeros, "zeros", torch.uint8), _stream()))
+    else:
+        _check("awq_quantize_pack_clip", lib().awq_quantize_pack_clip(
+            _dev(W, "W"), _dtype_code(W), out, n_in, _dev(s, "s", torch.float32),
+            _dev(clip, "clip", torch.float32), bits, group, _MODE[mode], _dev(qweight, "qweight"),
+            _dev(scales, "scales", torch.float32), _dev(zeros, "zeros", torch.uint8), _stream()))
     return qweight, scales, zeros
 
 
-def quantize_layer(W, X, bits=4, group=128, grid=20, mode="sym"):
+def quantize_layer(W, X, bits=4, group=128, grid=20, mode="sym", n_clip=0, max_shrink=0.5):
     """The whole path for one layer (or one stacked group of layers that share
-    X): statistics, search, final quantization and packing."""
+    X): statistics, search, final quantization and packing; with n_clip > 0 a
+    clipping-range search on W diag(s_best) runs before the packing."""
     xmag = act_stats(X)
     mse, best, s_best = search(W, X, xmag, bits, group, grid, mode)
-    qweight, scales, zeros = quantize_pack(W, s_best, bits, group, mode)
-    return {"xmag": xmag, "mse": mse, "best": best, "s_best": s_best,
+    clip = None
+    if n_clip > 0:
+        clip, _ = clip_search(W, X, s_best, bits, group, mode, n_clip, max_shrink)
+    qweight, scales, zeros = quantize_pack(W, s_best, bits, group, mode, clip=clip)
+    return {"xmag": xmag, "mse": mse, "best": best, "s_best": s_best, "clip": clip,
             "qweight": qweight, "scales": scales, "zeros": zeros}
 
 

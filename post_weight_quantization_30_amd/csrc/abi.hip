@@ -191,6 +191,30 @@ int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const f
                       int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros,
                       void *stream)
 {
+    return awq_quantize_pack_clip(W, dtype, out, in, s, nullptr, bits, group, mode, qweight, scales,
+                                  zeros, stream);
+}
+
+int awq_clip_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                    int64_t tokens, const float *s, int bits, int group, int mode, int n_clip,
+                    float max_shrink, float *clip, double *sse, void *stream)
+{
+    if (!s || !clip || out < 1 || in < 1 || tokens < 1 || n_clip < 1 || n_clip > AWQ_MAX_CLIP ||
+        !(max_shrink >= 0.0f && max_shrink < 1.0f))
+        return AWQ_ERR_INVALID_ARG;
+    int st = check_candidates(W, X, dtype, in, bits, group, mode);
+    if (st != AWQ_OK)
+        return st;
+    if (!search_group_ok(group) || in / group > 65535 || (out + 15) / 16 > (int64_t)0x7fffffff)
+        return AWQ_ERR_UNSUPPORTED;
+    return hip_status(awq::launch_clip_search(W, X, dtype, out, in, tokens, s, bits, group, mode,
+                                              n_clip, max_shrink, clip, sse, (hipStream_t)stream));
+}
+
+int awq_quantize_pack_clip(const void *W, int dtype, int64_t out, int64_t in, const float *s,
+                           const float *clip, int bits, int group, int mode, uint32_t *qweight,
+                           float *scales, uint8_t *zeros, void *stream)
+{
     if (!W || !s || !qweight || !scales || !zeros)
         return AWQ_ERR_INVALID_ARG;
     if (out < 1 || in < 1 || group < 1 || in % group != 0 || bits < 2 || bits > 8 ||
@@ -200,8 +224,8 @@ int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const f
         return AWQ_ERR_UNSUPPORTED;
     if ((out * (in / 32) + 255) / 256 > (int64_t)0x7fffffff)
         return AWQ_ERR_UNSUPPORTED;
-    return hip_status(awq::launch_pack(W, dtype, out, in, s, bits, group, mode, qweight, scales,
-                                       zeros, (hipStream_t)stream));
+    return hip_status(awq::launch_pack(W, dtype, out, in, s, clip, bits, group, mode, qweight,
+                                       scales, zeros, (hipStream_t)stream));
 }
 
 }  // extern "C"

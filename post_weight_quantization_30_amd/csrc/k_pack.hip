@@ -9,6 +9,10 @@
 //   and rtn under "GPTQ: compensate the error you just made"):
 //     lo = min(min v, 0), hi = max(max v, 0), scale = max((hi - lo) / maxq, 1e-8),
 //     zero = rne(-lo / scale), code = clamp(rne(v / scale) + zero, 0, maxq)
+// With clipping ratios r (one per row and group, from the clipping-range
+// search) the group's range is scaled first -- symmetric [-r max|v|, r max|v|],
+// asymmetric [r lo, r hi] -- v is clamped into it, and the scale (and zero)
+// are those of the scaled range; r = 1 gives the unclipped quantizer exactly.
 // Every quotient is the correctly rounded one (an IEEE division per group for
 // the reciprocal, two fma residual steps per weight), the library is built
 // with -ffp-contract=off and rintf is v_rndne_f32.
@@ -96,9 +100,10 @@ __device__ __forceinline__ void codes(const float (&v)[32], float scale, float l
     }
 }
 
-template <typename T, int BITS>
+template <typename T, int BITS, bool CLIP>
 __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, int64_t out,
                                                         int64_t in, const float *__restrict__ s,
+                                                        const float *__restrict__ clip,
                                                         int lanes_per_group, int mode,
                                                         uint32_t *__restrict__ qweight,
                                                         float *__restrict__ scales,
@@ -139,6 +144,9 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
             v[i] = 0.f;
     }
 
+    // Clamping into the clipped range keeps |x| / scale (and x / scale above
+    // lo / scale) within the bounds the FAST code path relies on.
+    const float ratio = CLIP ? clip[row * (chunks / lanes_per_group) + ch / lanes_per_group] : 1.0f;
     uint32_t word[BITS];
     float scale, zero;
     if (mode == AWQ_SYM) {
@@ -149,6 +157,12 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
             m = fmaxf(fmaxf(m, fabsf(v[i])), fabsf(v[i + 1]));
         for (int off = 1; off < lanes_per_group; off <<= 1)
             m = fmaxf(m, __shfl_xor(m, off));
+        if (CLIP) {
+            m = ratio * m;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                v[i] = fminf(fmaxf(v[i], -m), m);
+        }
         scale = fmaxf(m / levels, 1e-8f);
         zero = (float)(1 << (BITS - 1));
         if (scale <= FLT_MAX)
@@ -166,6 +180,13 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
         for (int off = 1; off < lanes_per_group; off <<= 1) {
             lo = fminf(lo, __shfl_xor(lo, off));
             hi = fmaxf(hi, __shfl_xor(hi, off));
+        }
+        if (CLIP) {
+            lo = ratio * lo;
+            hi = ratio * hi;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                v[i] = fminf(fmaxf(v[i], lo), hi);
         }
         scale = fmaxf((hi - lo) / maxq, 1e-8f);
         zero = rintf(-lo / scale);
@@ -188,15 +209,16 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, 
     }
 }
 
-template <typename T>
-static void pack_typed(const T *W, int64_t out, int64_t in, const float *s, int bits, int lpg, int mode,
-                       uint32_t *qweight, float *scales, uint8_t *zeros, hipStream_t st)
+template <typename T, bool CLIP>
+static void pack_typed(const T *W, int64_t out, int64_t in, const float *s, const float *clip,
+                       int bits, int lpg, int mode, uint32_t *qweight, float *scales,
+                       uint8_t *zeros, hipStream_t st)
 {
     const int64_t threads = out * (in / 32);
     dim3 grid((unsigned)((threads + 255) / 256));
-#define AWQ_PACK_LAUNCH(B)                                                                        \
-    hipLaunchKernelGGL((k_quantize_pack<T, B>), grid, dim3(256), 0, st, W, out, in, s, lpg, mode, \
-                       qweight, scales, zeros)
+#define AWQ_PACK_LAUNCH(B)                                                                   \
+    hipLaunchKernelGGL((k_quantize_pack<T, B, CLIP>), grid, dim3(256), 0, st, W, out, in, s, \
+                       clip, lpg, mode, qweight, scales, zeros)
     switch (bits) {
     case 2: AWQ_PACK_LAUNCH(2); break;
     case 3: AWQ_PACK_LAUNCH(3); break;
@@ -209,20 +231,31 @@ static void pack_typed(const T *W, int64_t out, int64_t in, const float *s, int 
 #undef AWQ_PACK_LAUNCH
 }
 
-hipError_t launch_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s, int bits,
-                       int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros,
-                       hipStream_t st)
+template <typename T>
+static void pack_clip_or_not(const T *W, int64_t out, int64_t in, const float *s, const float *clip,
+                             int bits, int lpg, int mode, uint32_t *qweight, float *scales,
+                             uint8_t *zeros, hipStream_t st)
+{
+    if (clip)
+        pack_typed<T, true>(W, out, in, s, clip, bits, lpg, mode, qweight, scales, zeros, st);
+    else
+        pack_typed<T, false>(W, out, in, s, clip, bits, lpg, mode, qweight, scales, zeros, st);
+}
+
+hipError_t launch_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s,
+                       const float *clip, int bits, int group, int mode, uint32_t *qweight,
+                       float *scales, uint8_t *zeros, hipStream_t st)
 {
     const int lpg = group / 32;
     switch (dtype) {
     case AWQ_F32:
-        pack_typed((const float *)W, out, in, s, bits, lpg, mode, qweight, scales, zeros, st);
+        pack_clip_or_not((const float *)W, out, in, s, clip, bits, lpg, mode, qweight, scales, zeros, st);
         break;
     case AWQ_F16:
-        pack_typed((const f16 *)W, out, in, s, bits, lpg, mode, qweight, scales, zeros, st);
+        pack_clip_or_not((const f16 *)W, out, in, s, clip, bits, lpg, mode, qweight, scales, zeros, st);
         break;
     default:
-        pack_typed((const bf16 *)W, out, in, s, bits, lpg, mode, qweight, scales, zeros, st);
+        pack_clip_or_not((const bf16 *)W, out, in, s, clip, bits, lpg, mode, qweight, scales, zeros, st);
         break;
     }
     return hipGetLastError();

@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search", "awq_quantize_pack", "awq_s_table",
+              "awq_clip_search", "awq_quantize_pack_clip",
               "awq_act_stats_workspace_size", "awq_search_workspace_size", "awq_status_string"):
         assert n in names
 
@@ -99,6 +100,45 @@ def _pack(L, **kw):
 ])
 def test_pack_rejects_bad_arguments(L, kw, status):
     assert _pack(L, **kw) == status
+
+
+def _pack_clip(L, **kw):
+    a = dict(W=FAKE, dtype=2, out=8, inn=256, s=FAKE, clip=FAKE, bits=4, group=128, mode=1,
+             q=FAKE, sc=FAKE, z=FAKE, stream=None)
+    a.update(kw)
+    return L.awq_quantize_pack_clip(a["W"], a["dtype"], a["out"], a["inn"], a["s"], a["clip"],
+                                    a["bits"], a["group"], a["mode"], a["q"], a["sc"], a["z"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), -1), (dict(s=None), -1), (dict(q=None), -1), (dict(sc=None), -1),
+    (dict(z=None), -1), (dict(out=0), -1), (dict(group=100), -1), (dict(bits=9), -1),
+    (dict(dtype=3), -1), (dict(mode=-1), -1), (dict(group=16, inn=256), -5),
+])
+def test_pack_clip_rejects_bad_arguments(L, kw, status):
+    assert _pack_clip(L, **kw) == status
+
+
+def _clip(L, **kw):
+    a = dict(W=FAKE, X=FAKE, dtype=1, out=64, inn=256, tokens=32, s=FAKE, bits=4, group=128,
+             mode=0, n_clip=20, shrink=0.5, clip=FAKE, sse=None, stream=None)
+    a.update(kw)
+    return L.awq_clip_search(a["W"], a["X"], a["dtype"], a["out"], a["inn"], a["tokens"], a["s"],
+                             a["bits"], a["group"], a["mode"], a["n_clip"], a["shrink"],
+                             a["clip"], a["sse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), -1), (dict(X=None), -1), (dict(s=None), -1), (dict(clip=None), -1),
+    (dict(out=0), -1), (dict(inn=0), -1), (dict(tokens=0), -1), (dict(group=96), -1),
+    (dict(bits=1), -1), (dict(bits=9), -1), (dict(dtype=5), -1), (dict(mode=2), -1),
+    (dict(n_clip=0), -1), (dict(n_clip=65), -1), (dict(shrink=-0.1), -1), (dict(shrink=1.0), -1),
+    (dict(shrink=float("nan")), -1),
+    (dict(group=256), -5), (dict(group=32, inn=32 * 65536), -5),   # valid, not in the GPU kernel
+])
+def test_clip_search_rejects_bad_arguments(L, kw, status):
+    assert _clip(L, **kw) == status
 
 
 def test_stats_and_s_table_reject_bad_arguments(L):

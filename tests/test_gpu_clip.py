@@ -1,0 +1,242 @@
+"""Clipping-range search and clipped packing on the GPU against the oracle.
+
+Bars:
+  * clipped pack (codes, scales, zeros): bitwise for the same s and ratios;
+  * per-(row, group, ratio) errors: within a bound derived from the kernel's
+    arithmetic (below), evaluated from the oracle's own quantities;
+  * chosen ratio: the oracle's, unless the oracle's errors at the two picks
+    differ by less than the two bounds together (a tie within rounding).
+
+Error bound. The kernel forms d = Wq - W in fp32 (3 roundings, relative),
+multiplies X by d in fp32 MFMA steps of 4 products each, accumulating over a
+group of G columns (at most 5 roundings per step, each relative to a partial
+sum bounded by sum_j |x_j d_j|), and sums squares in fp64. Per token
+    |y_gpu - y| <= delta = (2 G + 8) u sum_j |x_tj d_j|,   u = 2^-24,
+(the constant rounds 5 G / 4 + 3 up generously) and so per group
+    |sse_gpu - sse| <= sum_t (2 |y_t| delta_t + delta_t^2).
+Each test prints the case it runs (flushed) before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from post_weight_quantization_30_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def awq():
+    from post_weight_quantization_30_amd import awq as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()
+    return m
+
+
+def dev(arr, dtype):
+    from post_weight_quantization_30_amd import awq as m
+    return m.to_device(arr, dtype)
+
+
+def f32(arr, dtype):
+    return synth.storage_to_f32(arr, dtype)
+
+
+def sse_bounds(ref, Wf, Xf, s, bits, group, mode, n_clip, max_shrink):
+    """Per (row, group, ratio): the oracle's exact error and the bound above."""
+    out, n_in = Wf.shape
+    ng = n_in // group
+    X64 = Xf.astype(np.float64)
+    ratios = [ref.clip_ratio(i, n_clip, max_shrink) for i in range(n_clip)]
+    exact = np.empty((out, ng, n_clip))
+    bound = np.empty((out, ng, n_clip))
+    c = 2 * group + 8
+    for o in range(out):
+        for g in range(ng):
+            cols = slice(g * group, (g + 1) * group)
+            w = Wf[o, cols]
+            sg = s[cols]
+            v = (w * sg).astype(np.float32)
+            D = np.empty((n_clip, group))
+            for i, r in enumerate(ratios):
+                _, _, _, what = ref.quant_group_clip(v, bits, mode, r)
+                D[i] = what.astype(np.float64) / sg.astype(np.float64) - w.astype(np.float64)
+            Xg = X64[:, cols]
+            Y = Xg @ D.T
+            delta = c * U * (np.abs(Xg) @ np.abs(D).T)
+            exact[o, g] = (Y * Y).sum(axis=0)
+            bound[o, g] = (2 * np.abs(Y) * delta + delta * delta).sum(axis=0)
+    return exact, bound
+
+
+def check_clip(clip_g, sse_g, clip_o, sse_o, exact, bound, n_clip, max_shrink, ref, label):
+    # the oracle's fp64 errors and the bound's exact errors agree closely
+    assert np.allclose(sse_o, exact, rtol=1e-9, atol=1e-300)
+    err = np.abs(sse_g - sse_o)
+    worst = float((err / np.maximum(bound, 1e-300)).max())
+    diff = clip_g != clip_o
+    say(label, "max err/bound", worst, "choices differing", int(diff.sum()), "of", clip_g.size)
+    assert np.all(err <= bound), f"{label}: sse outside bound ({worst:.3g} x)"
+    ratios = np.array([ref.clip_ratio(i, n_clip, max_shrink) for i in range(n_clip)], np.float32)
+    assert np.all(np.isin(clip_g, ratios)), f"{label}: ratio outside the grid"
+    if diff.any():
+        idx = np.argwhere(diff)
+        for o, g in idx:
+            ig = int(np.nonzero(ratios == clip_g[o, g])[0][0])
+            io = int(np.nonzero(ratios == clip_o[o, g])[0][0])
+            gap = sse_o[o, g, ig] - sse_o[o, g, io]
+            assert gap <= bound[o, g, ig] + bound[o, g, io], \
+                f"{label}: row {o} group {g} picks {ig}, oracle {io}, gap {gap:.3e}"
+    # the GPU's pick is the first strict minimum of its own errors
+    first = np.argmin(sse_g, axis=-1)
+    assert np.array_equal(clip_g, ratios[first])
+
+
+CLIP_CASES = [
+    # (name, out, in, tokens, dtype, bits, group, mode, n_clip, max_shrink, seed)
+    ("f16 sym g128, ragged rows and tokens", 40, 512, 300, "f16", 4, 128, "sym", 20, 0.5, 11),
+    ("bf16 asym g128", 33, 256, 257, "bf16", 4, 128, "asym", 20, 0.5, 12),
+    ("f32 sym 3-bit g64", 17, 256, 100, "f32", 3, 64, "sym", 20, 0.5, 13),
+    ("bf16 asym 2-bit g32, one token", 16, 128, 1, "bf16", 2, 32, "asym", 20, 0.5, 14),
+    ("f16 sym 8-bit g32", 48, 256, 64, "f16", 8, 32, "sym", 20, 0.5, 15),
+    ("f16 asym 5-bit g64, 64 ratios", 24, 256, 48, "f16", 5, 64, "asym", 64, 0.9, 16),
+    ("bf16 sym g128, 13 ratios", 16, 384, 520, "bf16", 4, 128, "sym", 13, 0.3, 17),
+    ("f32 asym g32, one ratio", 5, 64, 20, "f32", 4, 32, "asym", 1, 0.5, 18),
+]
+
+
+def make_case(out, n_in, T, dt, bits, group, mode, seed):
+    spec = synth.with_shape(synth.CONFIGS[2], out=out, inn=n_in, tokens=T, seed=seed, dtype=dt,
+                            bits=bits, group=group, mode=mode)
+    lay = synth.make_layer(spec)
+    r = np.random.default_rng(seed)
+    s = np.exp(r.uniform(-1.5, 1.5, n_in)).astype(np.float32)
+    return lay, s
+
+
+@pytest.mark.parametrize("case", range(len(CLIP_CASES)))
+def test_clip_search_matches_oracle(awq, ref, case):
+    name, out, n_in, T, dt, bits, group, mode, n_clip, ms, seed = CLIP_CASES[case]
+    lay, s = make_case(out, n_in, T, dt, bits, group, mode, seed)
+    Wf, Xf = f32(lay["W"], dt), f32(lay["X"], dt)
+    clip_o, sse_o = ref.clip_search(Wf, Xf, s, bits, group, mode, n_clip, ms)
+    exact, bound = sse_bounds(ref, Wf, Xf, s, bits, group, mode, n_clip, ms)
+    say("clip search", name)
+    Wd, Xd, sd = dev(lay["W"], dt), dev(lay["X"], dt), torch.from_numpy(s).cuda()
+    clip_g, sse_g = awq.clip_search(Wd, Xd, sd, bits, group, mode, n_clip, ms, want_sse=True)
+    torch.cuda.synchronize()
+    clip_g, sse_g = clip_g.cpu().numpy(), sse_g.cpu().numpy()
+    check_clip(clip_g, sse_g, clip_o, sse_o, exact, bound, n_clip, ms, ref, name)
+    # without the sse output the same choices (bitwise reproducible)
+    clip_2, _ = awq.clip_search(Wd, Xd, sd, bits, group, mode, n_clip, ms)
+    torch.cuda.synchronize()
+    assert np.array_equal(clip_2.cpu().numpy(), clip_g)
+    # packing with the chosen ratios: bitwise with the oracle given the same ratios
+    q, sc, z = awq.quantize_pack(Wd, sd, bits, group, mode, clip=torch.from_numpy(clip_g).cuda())
+    torch.cuda.synchronize()
+    q_o, sc_o, z_o = ref.quantize_pack_clip(Wf, s, clip_g, bits, group, mode)
+    assert np.array_equal(q.cpu().numpy().view(np.uint32), q_o)
+    assert np.array_equal(sc.cpu().numpy(), sc_o)
+    assert np.array_equal(z.cpu().numpy(), z_o)
+
+
+def test_clip_search_degenerate_groups(awq, ref):
+    """All-zero rows tie at every ratio (first wins: no clipping); with
+    max_shrink = 0 every ratio is 1 and no group is clipped."""
+    out, n_in, T = 32, 256, 40
+    r = np.random.default_rng(5)
+    W = (r.standard_normal((out, n_in)) * 0.02).astype(np.float32)
+    W[3] = 0.0
+    W[17, 128:] = 0.0
+    X = r.standard_normal((T, n_in)).astype(np.float32)
+    s = np.exp(r.uniform(-1, 1, n_in)).astype(np.float32)
+    say("clip search degenerate groups")
+    Wd, Xd, sd = (torch.from_numpy(a).cuda() for a in (W, X, s))
+    for mode in ("sym", "asym"):
+        clip_g, sse_g = awq.clip_search(Wd, Xd, sd, 4, 128, mode, 20, 0.5, want_sse=True)
+        torch.cuda.synchronize()
+        clip_g, sse_g = clip_g.cpu().numpy(), sse_g.cpu().numpy()
+        assert np.all(sse_g[3] == 0.0) and np.all(clip_g[3] == 1.0)
+        assert np.all(sse_g[17, 1] == 0.0) and clip_g[17, 1] == 1.0
+        clip_o, _ = ref.clip_search(W, X, s, 4, 128, mode, 20, 0.5)
+        assert clip_o[3].tolist() == [1.0, 1.0] and clip_o[17, 1] == 1.0
+        c0, e0 = awq.clip_search(Wd, Xd, sd, 4, 128, mode, 8, 0.0, want_sse=True)
+        torch.cuda.synchronize()
+        e0 = e0.cpu().numpy()
+        assert np.all(c0.cpu().numpy() == 1.0)
+        assert np.all(e0 == e0[..., :1])
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mode", ["sym", "asym"])
+@pytest.mark.parametrize("bits,group", [(4, 128), (3, 64), (2, 32), (8, 256), (5, 2048)])
+def test_quantize_pack_clip_bitwise(awq, ref, dt, mode, bits, group):
+    """Random ratios in (0, 1] (ones included) through the clipped pack."""
+    n_in = max(group, 512) if group < 2048 else 4096
+    out = 37
+    say("pack clip", dt, mode, bits, group, n_in)
+    spec = synth.LayerSpec("p", out, n_in, 1, dt, bits, group, 1, mode, 900 + bits + group)
+    lay = synth.make_layer(spec)
+    r = np.random.default_rng(bits * group + 1)
+    s = np.exp(r.uniform(-2, 2, n_in)).astype(np.float32)
+    clip = r.uniform(0.05, 1.0, (out, n_in // group)).astype(np.float32)
+    clip[r.random(clip.shape) < 0.25] = 1.0
+    Wd, sd = dev(lay["W"], dt), torch.from_numpy(s).cuda()
+    q, sc, z = awq.quantize_pack(Wd, sd, bits, group, mode, clip=torch.from_numpy(clip).cuda())
+    torch.cuda.synchronize()
+    Wf = f32(lay["W"], dt)
+    q_o, sc_o, z_o = ref.quantize_pack_clip(Wf, s, clip, bits, group, mode)
+    assert np.array_equal(q.cpu().numpy().view(np.uint32), q_o)
+    assert np.array_equal(sc.cpu().numpy(), sc_o)
+    assert np.array_equal(z.cpu().numpy(), z_o)
+    # ratio 1 everywhere is the unclipped pack, bit for bit
+    ones = torch.ones((out, n_in // group), dtype=torch.float32, device="cuda")
+    q1, sc1, z1 = awq.quantize_pack(Wd, sd, bits, group, mode, clip=ones)
+    q2, sc2, z2 = awq.quantize_pack(Wd, sd, bits, group, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(sc1, sc2) and torch.equal(z1, z2)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_clip_search_full_size(awq, ref, cfg):
+    """Full-size layer with the GPU's own s_best: sampled row tiles against the
+    oracle, and the row-independence of the result (a slice of rows gives
+    the same choices as the whole layer)."""
+    spec = synth.CONFIGS[cfg]
+    say("clip full size", spec.name)
+    lay = synth.make_layer(spec)
+    Wd, Xd = dev(lay["W"], spec.dtype), dev(lay["X"], spec.dtype)
+    xm = awq.act_stats(Xd)
+    _, _, sb = awq.search(Wd, Xd, xm, spec.bits, spec.group, spec.grid, spec.mode)
+    clip_g, sse_g = awq.clip_search(Wd, Xd, sb, spec.bits, spec.group, spec.mode, 20, 0.5, want_sse=True)
+    torch.cuda.synchronize()
+    s = sb.cpu().numpy()
+    clip_g, sse_g = clip_g.cpu().numpy(), sse_g.cpu().numpy()
+    ratios = np.array([ref.clip_ratio(i, 20, 0.5) for i in range(20)], np.float32)
+    assert np.array_equal(clip_g, ratios[np.argmin(sse_g, axis=-1)])
+    # clipping never loses against no clipping (ratio 1 is a candidate)
+    assert np.all(sse_g.min(axis=-1) <= sse_g[..., 0])
+    Xf = f32(lay["X"], spec.dtype)
+    n = 8 if spec.inn * spec.tokens > 2 ** 25 else 16
+    for a in sorted({0, ((spec.out // 2) // 16) * 16 + 5, spec.out - n}):
+        b = a + n
+        Wf = f32(lay["W"][a:b], spec.dtype)
+        say("clip full size sample rows", spec.name, a, b)
+        clip_o, sse_o = ref.clip_search(Wf, Xf, s, spec.bits, spec.group, spec.mode, 20, 0.5)
+        exact, bound = sse_bounds(ref, Wf, Xf, s, spec.bits, spec.group, spec.mode, 20, 0.5)
+        check_clip(clip_g[a:b], sse_g[a:b], clip_o, sse_o, exact, bound, 20, 0.5, ref,
+                   f"{spec.name} rows {a}:{b}")
+        c2, e2 = awq.clip_search(Wd[a:b].contiguous(), Xd, sb, spec.bits, spec.group, spec.mode, 20,
+                                 0.5, want_sse=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(c2.cpu().numpy(), clip_g[a:b])
+        assert np.array_equal(e2.cpu().numpy(), sse_g[a:b])
