@@ -30,6 +30,8 @@ METRIC = "AWQ search: α-candidate·MACs/s + ms per layer (4096×4096, 256 tok, 
 SEARCH_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_search.hip")
 MFMA_PROBE = os.path.join(ROOT, "post_weight_quantization_30_amd", "mfma_peak")
 PMC_FILE = os.path.join(ROOT, "profiles", "k_search_linear_4096x4096_t256_hbm_counters.json")
+CLIP_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_clip.hip")
+CLIP_PMC_FILE = os.path.join(ROOT, "profiles", "k_clip_search_linear_4096x4096_t256_hbm_counters.json")
 
 
 def parse():
@@ -58,14 +60,15 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(config):
-    """HBM bytes per search launch from committed rocprofv3 counters, or None
-    when none are committed for this workload and the current kernel source."""
-    if not os.path.exists(PMC_FILE):
+def traffic_from_profile(config, pmc_file=PMC_FILE, src=SEARCH_SRC):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counters, or
+    None when none are committed for this workload and the current kernel source."""
+    if not os.path.exists(pmc_file):
         return None
-    with open(PMC_FILE) as f:
+    with open(pmc_file) as f:
         d = json.load(f)
-    if d.get("config") != config or d.get("k_search_source_sha256_16") != source_hash(SEARCH_SRC):
+    sha = d.get("source_sha256_16", d.get("k_search_source_sha256_16"))
+    if d.get("config") != config or sha != source_hash(src):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -155,7 +158,7 @@ def clip_measure(awq, torch, spec, W, X, s_best, args):
             "ratio_macs_per_s": macs / (ms * 1e-3),
             "roofline": {"bound": "mfma", "kernel": "k_clip_search", "achieved": achieved,
                          "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS,
-                         "traffic": None},
+                         "traffic": traffic_from_profile(spec.name, CLIP_PMC_FILE, CLIP_SRC)},
             "clipped_group_frac": float((clip < 1).float().mean().item()),
             "group_sse_vs_unclipped": float(e_best.sum() / e[..., 0].sum())}
 
