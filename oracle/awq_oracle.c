@@ -536,3 +536,90 @@ int awq_ref_quantize_pack_clip(const float *W, int64_t out, int64_t in, const fl
     free(code);
     return REF_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Folding s into the model ([G] "How it works" step 5 and the transformer
+ * paragraph; [C] "AWQ: move the error away from what matters": W is multiplied
+ * by s and the previous operation divided by it). The identity behind it is
+ * W x = (W diag(s)) (diag(s)^-1 x) ([C] "AWQ: move the error ..."; [G] "The
+ * code, line by line"). The pages do not say how the result is stored; here:
+ * one fp32 operation, then one rounding to the model's storage type.
+ * ------------------------------------------------------------------------- */
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+uint16_t awq_ref_f32_to_f16(float x)
+{
+    uint32_t b;
+    memcpy(&b, &x, sizeof b);
+    const uint32_t sign = (b >> 16) & 0x8000u;
+    const int32_t exp = (int32_t)((b >> 23) & 0xffu);
+    const uint32_t frac = b & 0x7fffffu;
+    if (exp == 0xff)                                   /* inf, NaN (kept quiet) */
+        return (uint16_t)(sign | 0x7c00u | (frac ? 0x200u | (frac >> 13) : 0u));
+    if (exp == 0)                                      /* fp32 zero or subnormal: < 2^-126 */
+        return (uint16_t)sign;
+    const uint32_t m = frac | 0x800000u;               /* value = m * 2^(exp - 150) */
+    const int32_t e16 = exp - 127 + 15;
+    if (e16 >= 31)
+        return (uint16_t)(sign | 0x7c00u);
+    uint32_t shift, q;
+    if (e16 >= 1) {
+        shift = 13;                                    /* keep 11 significant bits */
+        q = ((uint32_t)e16 << 10) | ((m >> 13) & 0x3ffu);
+    } else {
+        /* subnormal: units of 2^-24, value / 2^-24 = m * 2^(exp - 126) */
+        shift = (uint32_t)(126 - exp);
+        if (shift > 24)
+            return (uint16_t)sign;                     /* below a quarter unit */
+        q = m >> shift;
+    }
+    const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u)))
+        q += 1;                                        /* a carry moves up one binade (or to inf) */
+    return (uint16_t)(sign | q);
+}
+
+/* bfloat16: the upper half of the fp32 pattern, rounded half to even. */
+uint16_t awq_ref_f32_to_bf16(float x)
+{
+    uint32_t b;
+    memcpy(&b, &x, sizeof b);
+    if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x7fffffu))
+        return (uint16_t)((b >> 16) | 0x40u);          /* NaN, quiet */
+    const uint32_t lower = b & 0xffffu, upper = b >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        return (uint16_t)(upper + 1u);
+    return (uint16_t)upper;
+}
+
+static void store_one(void *out, int64_t i, int storage, float v)
+{
+    if (storage == AWQ_REF_STORE_F32)
+        ((float *)out)[i] = v;
+    else if (storage == AWQ_REF_STORE_F16)
+        ((uint16_t *)out)[i] = awq_ref_f32_to_f16(v);
+    else
+        ((uint16_t *)out)[i] = awq_ref_f32_to_bf16(v);
+}
+
+int awq_ref_fold_rows(const float *A, int64_t rows, int64_t cols, const float *s, int storage,
+                      void *out)
+{
+    if (!A || !s || !out || rows < 1 || cols < 1 || storage < 0 || storage > 2)
+        return REF_EINVAL;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            store_one(out, r * cols + c, storage, A[r * cols + c] / s[r]);
+    return REF_OK;
+}
+
+int awq_ref_scale_cols(const float *W, int64_t rows, int64_t cols, const float *s, int storage,
+                       void *out)
+{
+    if (!W || !s || !out || rows < 1 || cols < 1 || storage < 0 || storage > 2)
+        return REF_EINVAL;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            store_one(out, r * cols + c, storage, W[r * cols + c] * s[c]);
+    return REF_OK;
+}

@@ -114,6 +114,34 @@ int awq_ref_quantize_pack_clip(const float *W, int64_t out, int64_t in, const fl
                                const float *clip, int bits, int group, int mode,
                                uint32_t *qweight, float *scales, uint8_t *zeros);
 
+/* ---------------------------------------------------------------------------
+ * Folding the scales into the model ([G] "How it works" step 5 and the
+ * transformer paragraph after it; [C] "AWQ: move the error away from what
+ * matters"): the searched layer's weight becomes W diag(s), and 1/s is folded
+ * into whatever produces the layer's input -- a LayerNorm/RMSNorm weight (and
+ * bias), or the output rows of the previous linear layer (and its bias).
+ * Storage types: 0 fp32, 1 fp16, 2 bf16. Arithmetic is one fp32 operation per
+ * element (correctly rounded), then one round-half-to-even conversion to the
+ * storage type; out holds fp32 values (storage 0) or 16-bit patterns (1, 2).
+ * ------------------------------------------------------------------------- */
+enum { AWQ_REF_STORE_F32 = 0, AWQ_REF_STORE_F16 = 1, AWQ_REF_STORE_BF16 = 2 };
+
+/* fp32 -> IEEE binary16 / bfloat16 bit pattern, round half to even (overflow
+ * to infinity, gradual underflow to subnormals and zero; NaN stays NaN). */
+uint16_t awq_ref_f32_to_f16(float x);
+uint16_t awq_ref_f32_to_bf16(float x);
+
+/* Fold 1/s into a producer: out[r][c] = store(A[r][c] / s[r]) for A (rows, cols)
+ * whose row r produces input channel r of the searched layer (a norm weight
+ * is rows x 1). Returns 0 or -1. */
+int awq_ref_fold_rows(const float *A, int64_t rows, int64_t cols, const float *s, int storage,
+                      void *out);
+
+/* The searched layer's weight scaled: out[o][j] = store(W[o][j] * s[j]).
+ * Returns 0 or -1. */
+int awq_ref_scale_cols(const float *W, int64_t rows, int64_t cols, const float *s, int storage,
+                       void *out);
+
 #ifdef __cplusplus
 }
 #endif

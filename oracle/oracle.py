@@ -62,6 +62,14 @@ def _load():
     lib.awq_ref_quantize_pack_clip.argtypes = [f32p, i64, i64, f32p, ctypes.c_void_p, cint, cint, cint,
                                                u32p, f32p, u8p]
     lib.awq_ref_quantize_pack_clip.restype = cint
+    lib.awq_ref_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.awq_ref_f32_to_f16.restype = ctypes.c_uint16
+    lib.awq_ref_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.awq_ref_f32_to_bf16.restype = ctypes.c_uint16
+    lib.awq_ref_fold_rows.argtypes = [f32p, i64, i64, f32p, cint, ctypes.c_void_p]
+    lib.awq_ref_fold_rows.restype = cint
+    lib.awq_ref_scale_cols.argtypes = [f32p, i64, i64, f32p, cint, ctypes.c_void_p]
+    lib.awq_ref_scale_cols.restype = cint
     _lib = lib
     return lib
 
@@ -195,3 +203,37 @@ def quantize_pack_clip(W, s, clip, bits, group, mode):
     if st != 0:
         raise ValueError(f"awq_ref_quantize_pack_clip status {st}")
     return q, sc, z
+
+
+_STORE = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def f32_to_f16_bits(x):
+    """One fp32 value -> binary16 bit pattern (round half to even)."""
+    return int(_load().awq_ref_f32_to_f16(float(np.float32(x))))
+
+
+def f32_to_bf16_bits(x):
+    """One fp32 value -> bfloat16 bit pattern (round half to even)."""
+    return int(_load().awq_ref_f32_to_bf16(float(np.float32(x))))
+
+
+def _folded(fn, A, s, storage):
+    A = _f32(np.atleast_2d(A) if np.ndim(A) != 1 else A[:, None])
+    rows, cols = A.shape
+    out = np.empty((rows, cols), np.float32 if storage == "f32" else np.uint16)
+    st = fn(A, rows, cols, _f32(s), _STORE[storage], out.ctypes.data_as(ctypes.c_void_p))
+    if st != 0:
+        raise ValueError(f"fold status {st}")
+    return out
+
+
+def fold_rows(A, s, storage="f32"):
+    """store(A[r][c] / s[r]); A (rows, cols) or a vector (rows,) -> (rows, 1).
+    Returns fp32 values or 16-bit patterns (uint16) for f16 / bf16 storage."""
+    return _folded(_load().awq_ref_fold_rows, A, s, storage)
+
+
+def scale_cols(W, s, storage="f32"):
+    """store(W[o][j] * s[j])."""
+    return _folded(_load().awq_ref_scale_cols, W, s, storage)

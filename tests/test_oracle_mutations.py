@@ -50,8 +50,27 @@ CLIP_MUTATIONS = [
 ]
 
 
+# Mistakes in the scale folding and the storage conversions.
+FOLD_MUTATIONS = [
+ ("fold multiplies", "store_one(out, r * cols + c, storage, A[r * cols + c] / s[r]);",
+  "store_one(out, r * cols + c, storage, A[r * cols + c] * s[r]);"),
+ ("fold column index", "store_one(out, r * cols + c, storage, A[r * cols + c] / s[r]);",
+  "store_one(out, r * cols + c, storage, A[r * cols + c] / s[c % rows]);"),
+ ("scale divides", "store_one(out, r * cols + c, storage, W[r * cols + c] * s[c]);",
+  "store_one(out, r * cols + c, storage, W[r * cols + c] / s[c]);"),
+ ("f16 truncates", "if (rem > half || (rem == half && (q & 1u)))\n        q += 1;",
+  "if (0)\n        q += 1;"),
+ ("f16 ties away", "if (rem > half || (rem == half && (q & 1u)))", "if (rem >= half)"),
+ ("f16 flushes subnormals", "if (shift > 24)\n            return (uint16_t)sign;",
+  "if (shift > 0)\n            return (uint16_t)sign;"),
+ ("bf16 ties up", "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))",
+  "if (lower >= 0x8000u)"),
+]
+
+
 CASES = ([(n, b, a, "test_oracle_pins.py") for n, b, a in MUTATIONS] +
-         [(n, b, a, "test_oracle_clip_pins.py") for n, b, a in CLIP_MUTATIONS])
+         [(n, b, a, "test_oracle_clip_pins.py") for n, b, a in CLIP_MUTATIONS] +
+         [(n, b, a, "test_oracle_fold_pins.py") for n, b, a in FOLD_MUTATIONS])
 
 
 @pytest.mark.parametrize("name,before,after,pins", CASES, ids=[m[0] for m in CASES])
