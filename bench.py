@@ -163,6 +163,43 @@ def clip_measure(awq, torch, spec, W, X, s_best, args):
             "group_sse_vs_unclipped": float(e_best.sum() / e[..., 0].sum())}
 
 
+def fold_measure(awq, torch, spec, W, s_best, args):
+    """Folding s into the model: the previous linear layer's output rows / s
+    (a producer of the headline layer's shape and dtype stands in for it), the
+    layer's own columns * s, and a norm-weight vector. HBM roofline:
+    read and write every element once, plus s."""
+    out, n_in = spec.out, spec.inn
+    esize = W.element_size()
+    buf = torch.empty_like(W)
+    gamma = torch.ones(n_in, dtype=W.dtype, device=W.device)
+    gbuf = torch.empty_like(gamma)
+
+    def timed(fn, k):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    k = max(args.clip_steps, 10)
+    rows_ms = timed(lambda: awq.fold_rows(W, s_best, out=buf), k)
+    cols_ms = timed(lambda: awq.scale_cols(W, s_best, out=buf), k)
+    norm_ms = timed(lambda: awq.fold_rows(gamma, s_best, out=gbuf), k)
+    nbytes = 2 * out * n_in * esize + 4 * n_in
+    gbs = nbytes / (rows_ms * 1e-3) / 1e9
+    return {"producer_shape": [n_in, out], "rows_ms": rows_ms, "cols_ms": cols_ms,
+            "norm_vector_ms": norm_ms,
+            "roofline": {"bound": "hbm", "kernel": "k_fold_vec (rows)", "achieved": gbs,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": None},
+            "cols_gbs": nbytes / (cols_ms * 1e-3) / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -306,6 +343,7 @@ def main():
     }
     if not args.no_clip:
         rec["clip_search"] = clip_measure(awq, torch, spec, W, X, s_best, args)
+    rec["fold"] = fold_measure(awq, torch, spec, W, s_best, args)
     if args.copy_calib:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

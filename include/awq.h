@@ -198,6 +198,34 @@ int awq_quantize_pack_clip(const void *W, int dtype, int64_t out, int64_t in, co
                            const float *clip, int bits, int group, int mode, uint32_t *qweight,
                            float *scales, uint8_t *zeros, void *stream);
 
+/* Folding the scales into the model ("AWQ (activation-aware weight
+ * quantization)", "How it works" step 5 and the transformer paragraph after it;
+ * "AWQ vs GPTQ Quantization Architectures Compared", "AWQ: move the error away
+ * from what matters"). With W x = (W diag(s)) (diag(s)^-1 x), the searched
+ * layer's weight is multiplied by s and whatever produces its input is
+ * divided by s: the LayerNorm/RMSNorm weight (and bias) before q/k/v or
+ * gate/up, or the output rows of the previous linear layer (up_proj for
+ * down_proj; v_proj for o_proj only when its output width equals o_proj's
+ * input width -- with grouped-query attention it usually does not).
+ * One fp32 operation per element (IEEE), then one round-half-to-even
+ * conversion to `dtype`: bit-exact.
+ *   awq_fold_rows:  out[r][c] = A[r][c] / s[r]; A (rows, cols) is the producer
+ *                   (rows = the searched layer's input width; cols = 1 for a
+ *                   norm weight or bias vector).
+ *   awq_scale_cols: out[o][j] = W[o][j] * s[j]; W (rows, cols) is the searched
+ *                   layer (cols = its input width). awq_quantize_pack takes W
+ *                   and s directly; this call writes the scaled weights
+ *                   themselves (for export, or for another quantizer).
+ *   A / W, out: device, (rows, cols) of `dtype`; out may equal the input (in
+ *               place), otherwise the two must not overlap.
+ *   s:          device fp32, length rows (fold) or cols (scale).
+ * Non-finite or zero s gives the IEEE results (inf, NaN) in the affected
+ * elements; no error is reported. */
+int awq_fold_rows(const void *A, int dtype, int64_t rows, int64_t cols, const float *s, void *out,
+                  void *stream);
+int awq_scale_cols(const void *W, int dtype, int64_t rows, int64_t cols, const float *s, void *out,
+                   void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *awq_status_string(int status);
 

@@ -67,6 +67,10 @@ def lib():
         L.awq_quantize_pack_clip.argtypes = [vp, cint, i64, i64, vp, vp, cint, cint, cint, vp, vp,
                                              vp, vp]
         L.awq_quantize_pack_clip.restype = cint
+        L.awq_fold_rows.argtypes = [vp, cint, i64, i64, vp, vp, vp]
+        L.awq_fold_rows.restype = cint
+        L.awq_scale_cols.argtypes = [vp, cint, i64, i64, vp, vp, vp]
+        L.awq_scale_cols.restype = cint
         L.awq_status_string.argtypes = [cint]
         L.awq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -226,6 +230,45 @@ def quantize_pack(W, s, bits, group, mode, qweight=None, scales=None, zeros=None
             _dev(clip, "clip", torch.float32), bits, group, _MODE[mode], _dev(qweight, "qweight"),
             _dev(scales, "scales", torch.float32), _dev(zeros, "zeros", torch.uint8), _stream()))
     return qweight, scales, zeros
+
+
+def _rows_cols(A):
+    if A.dim() == 1:
+        return A.shape[0], 1
+    if A.dim() != 2:
+        raise ValueError("expected a vector or a matrix")
+    return A.shape[0], A.shape[1]
+
+
+def fold_rows(A, s, out=None):
+    """The producer of a searched layer's input absorbs 1/s: out[r] = A[r] / s[r]
+    for a norm weight or bias (vector) or the output rows of the previous
+    linear layer (matrix). out=A folds in place."""
+    rows, cols = _rows_cols(A)
+    if s.numel() != rows:
+        raise ValueError(f"the producer has {rows} output channels but s has {s.numel()}: it "
+                         "cannot absorb these scales (e.g. v_proj under grouped-query attention)")
+    out = torch.empty_like(A) if out is None else out
+    if out.shape != A.shape or out.dtype != A.dtype:
+        raise ValueError("out must match A")
+    _check("awq_fold_rows", lib().awq_fold_rows(
+        _dev(A, "A"), _dtype_code(A), rows, cols, _dev(s, "s", torch.float32), _dev(out, "out"),
+        _stream()))
+    return out
+
+
+def scale_cols(W, s, out=None):
+    """The searched layer's weight scaled: out[o][j] = W[o][j] * s[j]."""
+    rows, cols = _rows_cols(W)
+    if W.dim() != 2 or s.numel() != cols:
+        raise ValueError("W must be (out, in) and s of length in")
+    out = torch.empty_like(W) if out is None else out
+    if out.shape != W.shape or out.dtype != W.dtype:
+        raise ValueError("out must match W")
+    _check("awq_scale_cols", lib().awq_scale_cols(
+        _dev(W, "W"), _dtype_code(W), rows, cols, _dev(s, "s", torch.float32), _dev(out, "out"),
+        _stream()))
+    return out
 
 
 def quantize_layer(W, X, bits=4, group=128, grid=20, mode="sym", n_clip=0, max_shrink=0.5):

@@ -195,6 +195,32 @@ int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const f
                                   zeros, stream);
 }
 
+namespace {
+
+int fold_call(const void *A, int dtype, int64_t rows, int64_t cols, const float *s, void *out,
+              bool scale_cols, void *stream)
+{
+    if (!A || !s || !out || rows < 1 || cols < 1 || !valid_dtype(dtype))
+        return AWQ_ERR_INVALID_ARG;
+    if (rows > INT64_MAX / cols)
+        return AWQ_ERR_INVALID_ARG;
+    return hip_status(awq::launch_fold(A, dtype, rows, cols, s, out, scale_cols, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int awq_fold_rows(const void *A, int dtype, int64_t rows, int64_t cols, const float *s, void *out,
+                  void *stream)
+{
+    return fold_call(A, dtype, rows, cols, s, out, false, stream);
+}
+
+int awq_scale_cols(const void *W, int dtype, int64_t rows, int64_t cols, const float *s, void *out,
+                   void *stream)
+{
+    return fold_call(W, dtype, rows, cols, s, out, true, stream);
+}
+
 int awq_clip_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                     int64_t tokens, const float *s, int bits, int group, int mode, int n_clip,
                     float max_shrink, float *clip, double *sse, void *stream)

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search", "awq_quantize_pack", "awq_s_table",
-              "awq_clip_search", "awq_quantize_pack_clip",
+              "awq_clip_search", "awq_quantize_pack_clip", "awq_fold_rows", "awq_scale_cols",
               "awq_act_stats_workspace_size", "awq_search_workspace_size", "awq_status_string"):
         assert n in names
 
@@ -139,6 +139,18 @@ def _clip(L, **kw):
 ])
 def test_clip_search_rejects_bad_arguments(L, kw, status):
     assert _clip(L, **kw) == status
+
+
+@pytest.mark.parametrize("fn", ["awq_fold_rows", "awq_scale_cols"])
+def test_fold_rejects_bad_arguments(L, fn):
+    f = getattr(L, fn)
+    assert f(None, 1, 8, 8, FAKE, FAKE, None) == -1
+    assert f(FAKE, 1, 8, 8, None, FAKE, None) == -1
+    assert f(FAKE, 1, 8, 8, FAKE, None, None) == -1
+    assert f(FAKE, 1, 0, 8, FAKE, FAKE, None) == -1
+    assert f(FAKE, 1, 8, 0, FAKE, FAKE, None) == -1
+    assert f(FAKE, 3, 8, 8, FAKE, FAKE, None) == -1
+    assert f(FAKE, 1, 1 << 40, 1 << 40, FAKE, FAKE, None) == -1     # rows * cols overflows
 
 
 def test_stats_and_s_table_reject_bad_arguments(L):
