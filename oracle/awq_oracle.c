@@ -623,3 +623,50 @@ int awq_ref_scale_cols(const float *W, int64_t rows, int64_t cols, const float *
             store_one(out, r * cols + c, storage, W[r * cols + c] * s[c]);
     return REF_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Deployment: Y = X Wd^T with Wd the dequantized packed weights ([C] "What
+ * lands on disk": codes plus one scale and one zero per group and output row;
+ * "From checkpoint to kernel": the serving kernel consumes them directly).
+ * Dequantization is scale * (code - zero) (for symmetric layers the stored
+ * zero is 2^(bits-1)), taken exactly in fp64.
+ * ------------------------------------------------------------------------- */
+uint32_t awq_ref_unpack_code(const uint32_t *row, int64_t k, int bits)
+{
+    uint32_t code = 0;
+    for (int b = 0; b < bits; ++b) {
+        const uint64_t bit = (uint64_t)k * (uint64_t)bits + (uint64_t)b;
+        code |= ((row[bit / 32] >> (bit % 32)) & 1u) << b;
+    }
+    return code;
+}
+
+int awq_ref_qgemm(const float *X, int64_t M, int64_t in, const uint32_t *qweight,
+                  const float *scales, const uint8_t *zeros, int64_t out, int bits, int group,
+                  double *Y)
+{
+    if (!X || !qweight || !scales || !zeros || !Y || M < 1 ||
+        check_layer(out, in, bits, group, AWQ_REF_SYM) != REF_OK)
+        return REF_EINVAL;
+    const int64_t words = (in * bits + 31) / 32;
+    const int64_t ngroups = in / group;
+    double *wd = (double *)malloc((size_t)in * sizeof(double));
+    if (!wd)
+        return REF_EINVAL;
+    for (int64_t n = 0; n < out; ++n) {
+        const uint32_t *row = qweight + n * words;
+        for (int64_t k = 0; k < in; ++k) {
+            const int64_t g = k / group;
+            const double code = (double)awq_ref_unpack_code(row, k, bits);
+            wd[k] = (double)scales[n * ngroups + g] * (code - (double)zeros[n * ngroups + g]);
+        }
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < in; ++k)
+                acc += (double)X[m * in + k] * wd[k];
+            Y[m * out + n] = acc;
+        }
+    }
+    free(wd);
+    return REF_OK;
+}

@@ -142,6 +142,23 @@ int awq_ref_fold_rows(const float *A, int64_t rows, int64_t cols, const float *s
 int awq_ref_scale_cols(const float *W, int64_t rows, int64_t cols, const float *s, int storage,
                        void *out);
 
+/* ---------------------------------------------------------------------------
+ * The deployment consumer of the packed result ([C] "What lands on disk" and
+ * "From checkpoint to kernel": a serving kernel multiplies activations by the
+ * group-quantized weights; at decode batch sizes it is memory-bound). With the
+ * dequantized weight Wd[n][k] = scale[n][g] * (code[n][k] - zero[n][g]),
+ * g = k / group (exact in fp64):
+ *   Y[m][n] = sum_k X[m][k] * Wd[n][k]      (fp64, k ascending)
+ * X: (M, in) fp32 values; qweight / scales / zeros in the layout written by
+ * awq_ref_quantize_pack; Y: fp64 (M, out). Returns 0 or -1. */
+int awq_ref_qgemm(const float *X, int64_t M, int64_t in, const uint32_t *qweight,
+                  const float *scales, const uint8_t *zeros, int64_t out, int bits, int group,
+                  double *Y);
+
+/* Code k of one packed row: bits [k*bits, (k+1)*bits) of the row's
+ * little-endian stream of 32-bit words. */
+uint32_t awq_ref_unpack_code(const uint32_t *row, int64_t k, int bits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,10 @@ def _load():
     lib.awq_ref_fold_rows.restype = cint
     lib.awq_ref_scale_cols.argtypes = [f32p, i64, i64, f32p, cint, ctypes.c_void_p]
     lib.awq_ref_scale_cols.restype = cint
+    lib.awq_ref_qgemm.argtypes = [f32p, i64, i64, u32p, f32p, u8p, i64, cint, cint, f64p]
+    lib.awq_ref_qgemm.restype = cint
+    lib.awq_ref_unpack_code.argtypes = [u32p, i64, cint]
+    lib.awq_ref_unpack_code.restype = ctypes.c_uint32
     _lib = lib
     return lib
 
@@ -237,3 +241,21 @@ def fold_rows(A, s, storage="f32"):
 def scale_cols(W, s, storage="f32"):
     """store(W[o][j] * s[j])."""
     return _folded(_load().awq_ref_scale_cols, W, s, storage)
+
+
+def qgemm(X, qweight, scales, zeros, bits, group):
+    """Y (M, out) fp64 = X Wd^T with Wd = scale * (code - zero) from the packed layout."""
+    X = _f32(np.atleast_2d(X))
+    M, n_in = X.shape
+    q = np.ascontiguousarray(qweight).view(np.uint32)
+    out = q.shape[0]
+    Y = np.empty((M, out), np.float64)
+    st = _load().awq_ref_qgemm(X, M, n_in, np.ascontiguousarray(q), _f32(scales),
+                               np.ascontiguousarray(zeros, dtype=np.uint8), out, bits, group, Y)
+    if st != 0:
+        raise ValueError(f"awq_ref_qgemm status {st}")
+    return Y
+
+
+def unpack_code(row_words, k, bits):
+    return int(_load().awq_ref_unpack_code(np.ascontiguousarray(row_words, dtype=np.uint32), k, bits))

@@ -67,10 +67,24 @@ FOLD_MUTATIONS = [
   "if (lower >= 0x8000u)"),
 ]
 
+# Mistakes in the deployment product over the packed layout.
+QGEMM_MUTATIONS = [
+ ("unpack bit order", "code |= ((row[bit / 32] >> (bit % 32)) & 1u) << b;",
+  "code |= ((row[bit / 32] >> (31 - bit % 32)) & 1u) << b;"),
+ ("unpack stride", "const uint64_t bit = (uint64_t)k * (uint64_t)bits + (uint64_t)b;",
+  "const uint64_t bit = (uint64_t)k * 4u + (uint64_t)b;"),
+ ("qgemm no zero", "wd[k] = (double)scales[n * ngroups + g] * (code - (double)zeros[n * ngroups + g]);",
+  "wd[k] = (double)scales[n * ngroups + g] * code;"),
+ ("qgemm group index", "const int64_t g = k / group;", "const int64_t g = k % ngroups;"),
+ ("qgemm scale transposed", "wd[k] = (double)scales[n * ngroups + g] *",
+  "wd[k] = (double)scales[(g * out + n) % (out * ngroups)] *"),
+]
+
 
 CASES = ([(n, b, a, "test_oracle_pins.py") for n, b, a in MUTATIONS] +
          [(n, b, a, "test_oracle_clip_pins.py") for n, b, a in CLIP_MUTATIONS] +
-         [(n, b, a, "test_oracle_fold_pins.py") for n, b, a in FOLD_MUTATIONS])
+         [(n, b, a, "test_oracle_fold_pins.py") for n, b, a in FOLD_MUTATIONS] +
+         [(n, b, a, "test_oracle_qgemm_pins.py") for n, b, a in QGEMM_MUTATIONS])
 
 
 @pytest.mark.parametrize("name,before,after,pins", CASES, ids=[m[0] for m in CASES])
