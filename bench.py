@@ -200,6 +200,85 @@ def fold_measure(awq, torch, spec, W, s_best, args):
             "cols_gbs": nbytes / (cols_ms * 1e-3) / 1e9}
 
 
+def qgemm_measure(awq, torch, spec, X, qweight, scales, zeros, s_best, args):
+    """The deployment product over the layer's packed result: decode (1 and 16
+    tokens, HBM-bound: the packed weights are read once) and 256 tokens (MFMA).
+    Launches are captured in a HIP graph so that the host's per-call overhead
+    does not hide the kernel time; the graph's result is checked against an
+    eager call."""
+    out, n_in = spec.out, spec.inn
+    Xin = (X.float() / s_best[None, :]).to(X.dtype).contiguous()      # 1/s folded upstream
+    res = {}
+    for M in (1, 16, 256):
+        xm = Xin[:M].contiguous()
+        y = torch.empty((M, out), dtype=X.dtype, device=X.device)
+        awq.qgemm(xm, qweight, scales, zeros, spec.bits, spec.group, y=y)
+        torch.cuda.synchronize()
+        eager = y.clone()
+        reps = 20
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                awq.qgemm(xm, qweight, scales, zeros, spec.bits, spec.group, y=y)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k = max(1, args.clip_steps // 2)
+        e0.record()
+        for _ in range(k):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (k * reps)
+        if not torch.equal(y, eager):
+            raise RuntimeError("qgemm graph replay differs from the eager result")
+        ng = n_in // spec.group
+        nbytes = out * n_in * spec.bits / 8 + out * ng * 5 + M * n_in * 2 + M * out * 2
+        flops = 2.0 * M * n_in * out
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        tfs = flops / (ms * 1e-3) / 1e12
+        if M <= 16:
+            roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+        else:
+            roof = {"bound": "mfma", "achieved": tfs, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tfs / PEAK_F16_TFLOPS, "traffic": None}
+        res[f"M{M}"] = {"us": ms * 1e3, "bytes": nbytes, "gbs": gbs, "tflops": tfs, "roofline": roof}
+        del g
+    # decode on a wide layer (a gate/up-sized 28672 x 4096 int4 g128 stack,
+    # codes from a pack of seeded weights with s = 1): the transfer, not the
+    # launch and first round trip, dominates here
+    wo, wi, gw = 28672, 4096, 128
+    gen = torch.Generator(device=X.device).manual_seed(7)
+    Ww = (torch.randn((wo, wi), generator=gen, device=X.device) * 0.02).to(torch.float16)
+    qw, sw, zw = awq.quantize_pack(Ww, torch.ones(wi, dtype=torch.float32, device=X.device), 4, gw, "sym")
+    del Ww
+    xw = Xin[:1, :wi].to(torch.float16).contiguous()
+    yw = torch.empty((1, wo), dtype=torch.float16, device=X.device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(20):
+            awq.qgemm(xw, qw, sw, zw, 4, gw, y=yw)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 100
+    nbytes = wo * wi / 2 + wo * (wi // gw) * 5 + wi * 2 + wo * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res["M1_28672x4096"] = {"us": ms * 1e3, "bytes": nbytes, "gbs": gbs,
+                            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
+    del g
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -344,6 +423,8 @@ def main():
     if not args.no_clip:
         rec["clip_search"] = clip_measure(awq, torch, spec, W, X, s_best, args)
     rec["fold"] = fold_measure(awq, torch, spec, W, s_best, args)
+    if spec.dtype in ("f16", "bf16") and spec.bits in (4, 8) and spec.group in (32, 64, 128):
+        rec["qgemm"] = qgemm_measure(awq, torch, spec, X, qweight, scales, zeros, s_best, args)
     if args.copy_calib:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -226,6 +226,29 @@ int awq_fold_rows(const void *A, int dtype, int64_t rows, int64_t cols, const fl
 int awq_scale_cols(const void *W, int dtype, int64_t rows, int64_t cols, const float *s, void *out,
                    void *stream);
 
+/* The deployment product over the packed layout ("AWQ vs GPTQ Quantization
+ * Architectures Compared", "What lands on disk": codes plus one scale and one
+ * zero per group and output row; "From checkpoint to kernel": the serving
+ * kernel multiplies activations by them, memory-bound at decode):
+ *   Y[m][n] = sum_k X[m][k] * scale[n][k/group] * (code[n][k] - zero[n][k/group])
+ * X is the layer's input with 1/s already folded into its producer (see
+ * awq_fold_rows), so Y approximates the original layer's output.
+ *   X:        device (M, in) of x_dtype (AWQ_F16 or AWQ_BF16); 16-byte aligned.
+ *   qweight, scales, zeros: device, as written by awq_quantize_pack for an
+ *             (out, in) layer with these bits and group; qweight 16-byte aligned.
+ *   Y:        device (M, out) of y_dtype: AWQ_F32, or x_dtype (rounded to
+ *             nearest even from the fp32 result).
+ * Arithmetic: code - zero is exact in the 16-bit operand type; each group's
+ * products are summed in fp32 by the matrix cores and multiplied once by the
+ * group's scale into an fp32 total (fixed order, bitwise reproducible). Each
+ * output is within (group + ngroups + 8) * 2^-24 * sum_k |X[m][k] * Wd[n][k]| of
+ * the exact value (plus the final 16-bit rounding when y_dtype is 16-bit).
+ * AWQ_ERR_UNSUPPORTED: x_dtype AWQ_F32, bits not in {4, 8}, group not in
+ * {32, 64, 128}, a misaligned X or qweight, or M above 2 097 120. */
+int awq_qgemm(const void *X, int x_dtype, int64_t M, int64_t in, const uint32_t *qweight,
+              const float *scales, const uint8_t *zeros, int64_t out, int bits, int group,
+              void *Y, int y_dtype, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *awq_status_string(int status);
 

@@ -71,6 +71,8 @@ def lib():
         L.awq_fold_rows.restype = cint
         L.awq_scale_cols.argtypes = [vp, cint, i64, i64, vp, vp, vp]
         L.awq_scale_cols.restype = cint
+        L.awq_qgemm.argtypes = [vp, cint, i64, i64, vp, vp, vp, i64, cint, cint, vp, cint, vp]
+        L.awq_qgemm.restype = cint
         L.awq_status_string.argtypes = [cint]
         L.awq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -269,6 +271,25 @@ def scale_cols(W, s, out=None):
         _dev(W, "W"), _dtype_code(W), rows, cols, _dev(s, "s", torch.float32), _dev(out, "out"),
         _stream()))
     return out
+
+
+def qgemm(X, qweight, scales, zeros, bits, group, y=None, y_f32=False):
+    """Y (M, out) = X Wd^T with Wd = scale * (code - zero) read from the packed
+    layout (X: fp16 / bf16 (M, in) with 1/s folded upstream). Y is fp32 when
+    y_f32, else X's dtype."""
+    M, n_in = X.shape
+    out = qweight.shape[0]
+    if scales.shape != (out, n_in // group) or zeros.shape != scales.shape:
+        raise ValueError("scales / zeros must be (out, in / group)")
+    if qweight.shape[1] != words_per_row(n_in, bits):
+        raise ValueError("qweight has the wrong number of words per row")
+    ydt = torch.float32 if y_f32 else X.dtype
+    y = torch.empty((M, out), dtype=ydt, device=X.device) if y is None else y
+    _check("awq_qgemm", lib().awq_qgemm(
+        _dev(X, "X"), _dtype_code(X), M, n_in, _dev(qweight, "qweight"),
+        _dev(scales, "scales", torch.float32), _dev(zeros, "zeros", torch.uint8), out, bits, group,
+        _dev(y, "y", ydt), _DTYPE[ydt], _stream()))
+    return y
 
 
 def quantize_layer(W, X, bits=4, group=128, grid=20, mode="sym", n_clip=0, max_shrink=0.5):

@@ -221,6 +221,22 @@ int awq_scale_cols(const void *W, int dtype, int64_t rows, int64_t cols, const f
     return fold_call(W, dtype, rows, cols, s, out, true, stream);
 }
 
+int awq_qgemm(const void *X, int x_dtype, int64_t M, int64_t in, const uint32_t *qweight,
+              const float *scales, const uint8_t *zeros, int64_t out, int bits, int group, void *Y,
+              int y_dtype, void *stream)
+{
+    if (!X || !qweight || !scales || !zeros || !Y || M < 1 || in < 1 || out < 1 || group < 1 ||
+        in % group != 0 || bits < 2 || bits > 8 || !valid_dtype(x_dtype) || !valid_dtype(y_dtype) ||
+        (y_dtype != AWQ_F32 && y_dtype != x_dtype))
+        return AWQ_ERR_INVALID_ARG;
+    if (x_dtype == AWQ_F32 || (bits != 4 && bits != 8) || !search_group_ok(group) ||
+        (uintptr_t)X % 16 != 0 || (uintptr_t)qweight % 16 != 0 || M > 65535LL * 32 ||
+        (out + 15) / 16 > (int64_t)0x7fffffff)
+        return AWQ_ERR_UNSUPPORTED;
+    return hip_status(awq::launch_qgemm(X, x_dtype, M, in, qweight, scales, zeros, out, bits, group, Y,
+                                        y_dtype == AWQ_F32, (hipStream_t)stream));
+}
+
 int awq_clip_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                     int64_t tokens, const float *s, int bits, int group, int mode, int n_clip,
                     float max_shrink, float *clip, double *sse, void *stream)

@@ -85,6 +85,9 @@ hipError_t launch_reduce_argmin(const double *partial, int64_t nblk, int n_alpha
 hipError_t launch_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s,
                        const float *clip, int bits, int group, int mode, uint32_t *qweight,
                        float *scales, uint8_t *zeros, hipStream_t st);
+hipError_t launch_qgemm(const void *X, int dtype, int64_t M, int64_t in, const uint32_t *qweight,
+                        const float *scales, const uint8_t *zeros, int64_t out, int bits, int group,
+                        void *Y, bool yf32, hipStream_t st);
 hipError_t launch_fold(const void *A, int dtype, int64_t rows, int64_t cols, const float *s, void *out,
                        bool scale_cols, hipStream_t st);
 hipError_t launch_clip_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,

@@ -1,0 +1,416 @@
+// k_qgemm.hip -- the deployment product over the packed layout.
+//
+// Y[m][n] = sum_k X[m][k] * Wd[n][k],  Wd[n][k] = scale[n][g] * (code[n][k] - zero[n][g]),
+// g = k / group: the serving-side consumer of the quantized weights ("AWQ vs
+// GPTQ Quantization Architectures Compared", "What lands on disk" and "From
+// checkpoint to kernel": at decode batch sizes the layer is memory-bound and
+// the speed-up comes from reading a quarter of the bytes).
+//
+// Exactness: code - zero is a small integer, exact in fp16 and bf16, so the
+// MFMA multiplies X by exact integer-valued weights; each group's fp32 sum is
+// multiplied once by its scale (one fma into the fp32 total). No weight is
+// ever rounded to 16 bits.
+//
+// Layout: one block = (16 NT) output rows x (16 MT) tokens, 8 waves; wave w
+// takes groups w, w + 8, w + 16, ... (split-K inside the block, so a 4096-row
+// layer at decode still fills 256 blocks), and the 8 partial tiles are added
+// in wave order through LDS. The packed rows go through LDS so that the HBM
+// reads are whole cache lines (see QStage). In an MFMA k-step the four 8-wide k-slots of lane
+// group c hold columns c * G/4 + 8 s + e of the group (s = step, e = element),
+// for the X operand and for the codes alike, so a lane reads G/4 consecutive
+// codes of its row (whole 32-bit words) and G/4 consecutive activations.
+#include "awq_internal.h"
+
+#include <type_traits>
+
+namespace awq {
+
+constexpr int kQWaves = 8;
+
+template <typename TX> struct QOp;
+template <> struct QOp<f16> {
+    typedef f16x8 vec;
+    static __device__ __forceinline__ f32x4 mfma(const vec &a, const vec &b, const f32x4 &c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct QOp<bf16> {
+    typedef bf16x8 vec;
+    static __device__ __forceinline__ f32x4 mfma(const vec &a, const vec &b, const f32x4 &c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Per-block staging of the packed rows. A round covers 8 consecutive groups
+// (one per wave) of the block's R = 16 NT rows: RB = 8 G BITS / 8 bytes per
+// row, loaded with contiguous 16-byte chunks per lane (whole cache lines, a
+// wave covering one or more rows end to end), together with the round's
+// scales and zeros, and stored to LDS rows padded by 16 bytes (the 16 rows a
+// 16-byte LDS read touches then fall on distinct banks).
+template <int BITS, int G, int NT>
+struct QStage {
+    static constexpr int R = 16 * NT;
+    static constexpr int GB = G * BITS / 8;          // bytes of one group of one row
+    static constexpr int RB = 8 * GB;                // bytes of a round of one row
+    static constexpr int RBP = RB + 16;              // padded LDS row stride
+    static constexpr int CHUNKS = R * RB / 16;       // 16-byte chunks per round
+    static constexpr int PER_THREAD = (CHUNKS + kQWaves * 64 - 1) / (kQWaves * 64);
+    static constexpr int BUF = R * RBP + R * 8 * 4 + R * 8;   // codes, scales, zeros
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int BITS, int G, int NT>
+struct QRound {
+    typedef QStage<BITS, G, NT> S;
+    u32x4 chunk[S::PER_THREAD];
+    float scale;
+    uint8_t zero;
+};
+
+// Global -> registers for round q (every access in bounds: rows past `out`
+// are clamped, groups past ng are not loaded).
+template <int BITS, int G, int NT>
+__device__ __forceinline__ void q_fetch(QRound<BITS, G, NT> &rd, const uint8_t *qbytes, const float *scales,
+                                        const uint8_t *zeros, int64_t n0, int64_t out, int64_t ng,
+                                        int64_t row_bytes, int64_t q)
+{
+    typedef QStage<BITS, G, NT> S;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < S::PER_THREAD; ++k) {
+        const int ch = tid + k * kQWaves * 64;
+        if (ch < S::CHUNKS) {
+            const int row = ch / (S::RB / 16), off = (ch % (S::RB / 16)) * 16;
+            int64_t n = n0 + row;
+            n = n < out ? n : out - 1;
+            const int64_t byte = q * S::RB + off;
+            if (byte < row_bytes)
+                rd.chunk[k] = *reinterpret_cast<const u32x4 *>(qbytes + n * row_bytes + byte);
+        }
+    }
+    if (tid < S::R * 8) {
+        const int row = tid / 8, j = tid % 8;
+        int64_t n = n0 + row;
+        n = n < out ? n : out - 1;
+        const int64_t g = q * 8 + j;
+        if (g < ng) {
+            rd.scale = scales[n * ng + g];
+            rd.zero = zeros[n * ng + g];
+        }
+    }
+}
+
+template <int BITS, int G, int NT>
+__device__ __forceinline__ void q_stash(const QRound<BITS, G, NT> &rd, uint8_t *buf)
+{
+    typedef QStage<BITS, G, NT> S;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < S::PER_THREAD; ++k) {
+        const int ch = tid + k * kQWaves * 64;
+        if (ch < S::CHUNKS) {
+            const int row = ch / (S::RB / 16), off = (ch % (S::RB / 16)) * 16;
+            *reinterpret_cast<u32x4 *>(buf + row * S::RBP + off) = rd.chunk[k];
+        }
+    }
+    if (tid < S::R * 8) {
+        reinterpret_cast<float *>(buf + S::R * S::RBP)[tid] = rd.scale;
+        (buf + S::R * S::RBP + S::R * 8 * 4)[tid] = rd.zero;
+    }
+}
+
+// X fragments of one group for one lane (MT token tiles). Token rows past M
+// load the last row instead: their products only reach accumulator rows that
+// are never stored. (A zero fill on a per-lane branch would make the compiler
+// wait for the load at the join.)
+template <typename TX, int G, int MT>
+__device__ __forceinline__ void q_fetch_x(typename QOp<TX>::vec (&x)[MT][G / 32], const TX *X, int64_t M,
+                                          int64_t in, int64_t g, int64_t m0, int r, int c)
+{
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        int64_t m = m0 + t * 16 + r;
+        m = m < M ? m : M - 1;
+        const TX *xp = X + m * in + g * G + c * (G / 4);
+#pragma unroll
+        for (int s = 0; s < G / 32; ++s)
+            x[t][s] = load8(xp + 8 * s);
+    }
+}
+
+// (a & m) | o in one v_and_or_b32. The compiler splits it in two when m and
+// o are literals (a VOP3 instruction on this target takes no literal), so the
+// constants are passed in registers.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+    return r;
+}
+
+// fp16 operands: the eight codes of a k-step become (code - zero) two at a
+// time without leaving 16 bits. 0x6400 | c is the fp16 value 1024 + c
+// (c < 1024), so one mask-and-or makes a pair from two codes that sit 16 bits
+// apart in the code words, and one packed fp16 subtraction of 1024 + zero
+// leaves the exact small integers. The pairs come out in the order PERM
+// (4-bit: codes 0,4,1,5,2,6,3,7 of a word; 8-bit: 0,2,1,3 of each word), and
+// the X fragment is permuted the same way: the contraction over k does not
+// depend on the order in which both operands present it.
+template <int BITS> struct F16Pairs;
+template <> struct F16Pairs<4> {
+    static constexpr int PERM[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    static constexpr uint32_t kMask = 0x000F000Fu;
+    static __device__ __forceinline__ void make(const uint32_t *w, uint32_t (&u)[4], uint32_t mask,
+                                                uint32_t magic)
+    {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            u[p] = and_or(w[0] >> (4 * p), mask, magic);
+    }
+};
+template <> struct F16Pairs<8> {
+    static constexpr int PERM[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    static constexpr uint32_t kMask = 0x00FF00FFu;
+    static __device__ __forceinline__ void make(const uint32_t *w, uint32_t (&u)[4], uint32_t mask,
+                                                uint32_t magic)
+    {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            u[2 * q] = and_or(w[q], mask, magic);
+            u[2 * q + 1] = and_or(w[q] >> 8, mask, magic);
+        }
+    }
+};
+
+// One group for one wave: B fragments of its NT row tiles from the staged
+// round, X fragments from registers; each row tile's fp32 group sums are
+// scaled into the totals.
+template <typename TX, int BITS, int G, int MT, int NT>
+__device__ __forceinline__ void q_group(const uint8_t *buf, int w, const typename QOp<TX>::vec (&x)[MT][G / 32],
+                                        f32x4 (&acc)[MT][NT], int r, int c)
+{
+    typedef QStage<BITS, G, NT> S;
+    typedef typename QOp<TX>::vec vec;
+    constexpr int STEPS = G / 32;
+    constexpr int WPL = G * BITS / 128;              // code words per lane
+    constexpr uint32_t cmask = (1u << BITS) - 1u;
+    constexpr bool kPairs = std::is_same<TX, f16>::value;
+    vec xs[MT][STEPS];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            if constexpr (kPairs) {
+                constexpr const int *P = F16Pairs<BITS>::PERM;
+                xs[t][s] = __builtin_shufflevector(x[t][s], x[t][s], P[0], P[1], P[2], P[3], P[4], P[5],
+                                                   P[6], P[7]);
+            } else {
+                xs[t][s] = x[t][s];
+            }
+        }
+    const float *sbuf = reinterpret_cast<const float *>(buf + S::R * S::RBP);
+    const uint8_t *zbuf = buf + S::R * S::RBP + S::R * 8 * 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int row = nt * 16 + r;
+        uint32_t wv[WPL];
+        const uint8_t *src = buf + row * S::RBP + w * S::GB + c * (S::GB / 4);
+        if constexpr (WPL % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < WPL / 4; ++q) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 16 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    wv[4 * q + e] = v[e];
+            }
+        } else if constexpr (WPL == 2) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
+            wv[0] = v[0];
+            wv[1] = v[1];
+        } else {
+            wv[0] = *reinterpret_cast<const uint32_t *>(src);
+        }
+        const float scale = sbuf[row * 8 + w];
+        const int zero = zbuf[row * 8 + w];
+        vec b[STEPS];
+        if constexpr (kPairs) {
+            const f16 zb = static_cast<f16>(1024 + zero);           // exact: at most 1279
+            const f16x2 z2 = {zb, zb};
+            const uint32_t mask = F16Pairs<BITS>::kMask, magic = 0x64006400u;
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s) {
+                uint32_t u[4];
+                F16Pairs<BITS>::make(&wv[s * BITS / 4], u, mask, magic);    // the step's BITS/4 words
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const f16x2 d = __builtin_bit_cast(f16x2, u[p]) - z2;   // exact
+                    b[s][2 * p] = d[0];
+                    b[s][2 * p + 1] = d[1];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 8 * s + e;                // code j of the lane's G/4 codes
+                    const int code = (int)((wv[(j * BITS) / 32] >> ((j * BITS) % 32)) & cmask);
+                    b[s][e] = static_cast<TX>(static_cast<float>(code - zero));   // exact
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s)
+                part = QOp<TX>::mfma(xs[t][s], b[s], part);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][nt][i] = fmaf(scale, part[i], acc[t][nt][i]);
+        }
+    }
+}
+
+// Block: (16 NT) output rows x (16 MT) tokens, 8 waves; round q stages groups
+// 8q .. 8q+7 and wave w computes group 8q + w. Round q + 1 is fetched from
+// HBM (codes, scales, zeros, and each wave's X fragments) while round q is
+// computed; one barrier per round.
+template <typename TX, int BITS, int G, int MT, int NT, bool YF32>
+__global__ __launch_bounds__(kQWaves * 64) void k_qgemm(const TX *__restrict__ X, int64_t M, int64_t in,
+                                                        const uint32_t *__restrict__ qweight,
+                                                        const float *__restrict__ scales,
+                                                        const uint8_t *__restrict__ zeros, int64_t out,
+                                                        void *__restrict__ Y)
+{
+    typedef QStage<BITS, G, NT> S;
+    typedef typename QOp<TX>::vec vec;
+    constexpr int RED = kQWaves * MT * NT * 64 * 16;
+    constexpr int LDS = 2 * S::BUF > RED ? 2 * S::BUF : RED;
+    __shared__ __align__(16) uint8_t lds[LDS];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, c = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * S::R;
+    const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+    const int64_t ng = in / G;
+    const int64_t row_bytes = in * BITS / 8;
+    const int64_t rounds = (ng + 7) / 8;
+    const uint8_t *qbytes = reinterpret_cast<const uint8_t *>(qweight);
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    QRound<BITS, G, NT> rd = {};
+    vec xcur[MT][G / 32], xnext[MT][G / 32];
+    q_fetch(rd, qbytes, scales, zeros, n0, out, ng, row_bytes, 0);
+    if (wave < ng)
+        q_fetch_x<TX, G, MT>(xcur, X, M, in, wave, m0, r, c);
+    q_stash(rd, lds);
+    __syncthreads();
+    for (int64_t q = 0; q < rounds; ++q) {
+        const bool more = q + 1 < rounds;
+        const int64_t g = q * 8 + wave, gn = g + 8;
+        if (more) {
+            q_fetch(rd, qbytes, scales, zeros, n0, out, ng, row_bytes, q + 1);
+            if (gn < ng)
+                q_fetch_x<TX, G, MT>(xnext, X, M, in, gn, m0, r, c);
+        }
+        if (g < ng)
+            q_group<TX, BITS, G, MT, NT>(lds + (q & 1) * S::BUF, wave, xcur, acc, r, c);
+        if (more) {
+            q_stash(rd, lds + ((q + 1) & 1) * S::BUF);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int s = 0; s < G / 32; ++s)
+                    xcur[t][s] = xnext[t][s];
+        }
+        __syncthreads();
+    }
+
+    // fixed-order reduction over the waves (the staging buffers are free now)
+    f32x4 *red = reinterpret_cast<f32x4 *>(lds);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            red[((wave * MT + t) * NT + nt) * 64 + lane] = acc[t][nt];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < MT * NT * 64; idx += blockDim.x) {
+        const int t = idx / (NT * 64), nt = (idx / 64) % NT, l = idx & 63;
+        f32x4 sum = red[(t * NT + nt) * 64 + l];
+#pragma unroll
+        for (int w = 1; w < kQWaves; ++w)
+            sum += red[((w * MT + t) * NT + nt) * 64 + l];
+        const int64_t nn = n0 + nt * 16 + (l & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = m0 + t * 16 + 4 * (l >> 4) + i;
+            if (m < M && nn < out) {
+                if (YF32)
+                    static_cast<float *>(Y)[m * out + nn] = sum[i];
+                else
+                    static_cast<TX *>(Y)[m * out + nn] = static_cast<TX>(sum[i]);
+            }
+        }
+    }
+}
+
+template <typename TX, int BITS, int G>
+static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t *qweight,
+                           const float *scales, const uint8_t *zeros, int64_t out, void *Y, bool yf32,
+                           hipStream_t st)
+{
+    const dim3 block(kQWaves * 64);
+    // decode (M <= 16): 16 tokens and 16 rows per block, or 32 rows on layers
+    // with at least 8192 rows (twice the bytes staged per round; enough blocks
+    // remain to fill the chip); otherwise 64 rows x 32 tokens per block (each
+    // staged row and X fragment reused 4 and 2 times).
+#define AWQ_QGEMM(MT, NT, YF)                                                                        \
+    hipLaunchKernelGGL((k_qgemm<TX, BITS, G, MT, NT, YF>),                                            \
+                       dim3((unsigned)((out + 16 * NT - 1) / (16 * NT)),                             \
+                            (unsigned)((M + 16 * MT - 1) / (16 * MT))),                              \
+                       block, 0, st, (const TX *)X, M, in, qweight, scales, zeros, out, Y)
+    if (M <= 16 && out < 8192) {
+        if (yf32) AWQ_QGEMM(1, 1, true); else AWQ_QGEMM(1, 1, false);
+    } else if (M <= 16) {
+        if (yf32) AWQ_QGEMM(1, 2, true); else AWQ_QGEMM(1, 2, false);
+    } else {
+        if (yf32) AWQ_QGEMM(2, 4, true); else AWQ_QGEMM(2, 4, false);
+    }
+#undef AWQ_QGEMM
+    return hipGetLastError();
+}
+
+template <typename TX, int BITS>
+static hipError_t qgemm_g(const void *X, int64_t M, int64_t in, const uint32_t *qweight,
+                          const float *scales, const uint8_t *zeros, int64_t out, int group, void *Y,
+                          bool yf32, hipStream_t st)
+{
+    switch (group) {
+    case 32: return qgemm_mt<TX, BITS, 32>(X, M, in, qweight, scales, zeros, out, Y, yf32, st);
+    case 64: return qgemm_mt<TX, BITS, 64>(X, M, in, qweight, scales, zeros, out, Y, yf32, st);
+    default: return qgemm_mt<TX, BITS, 128>(X, M, in, qweight, scales, zeros, out, Y, yf32, st);
+    }
+}
+
+hipError_t launch_qgemm(const void *X, int dtype, int64_t M, int64_t in, const uint32_t *qweight,
+                        const float *scales, const uint8_t *zeros, int64_t out, int bits, int group,
+                        void *Y, bool yf32, hipStream_t st)
+{
+    if (dtype == AWQ_F16)
+        return bits == 4 ? qgemm_g<f16, 4>(X, M, in, qweight, scales, zeros, out, group, Y, yf32, st)
+                         : qgemm_g<f16, 8>(X, M, in, qweight, scales, zeros, out, group, Y, yf32, st);
+    return bits == 4 ? qgemm_g<bf16, 4>(X, M, in, qweight, scales, zeros, out, group, Y, yf32, st)
+                     : qgemm_g<bf16, 8>(X, M, in, qweight, scales, zeros, out, group, Y, yf32, st);
+}
+
+}  // namespace awq

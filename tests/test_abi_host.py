@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search", "awq_quantize_pack", "awq_s_table",
-              "awq_clip_search", "awq_quantize_pack_clip", "awq_fold_rows", "awq_scale_cols",
+              "awq_clip_search", "awq_quantize_pack_clip", "awq_fold_rows", "awq_scale_cols", "awq_qgemm",
               "awq_act_stats_workspace_size", "awq_search_workspace_size", "awq_status_string"):
         assert n in names
 
@@ -151,6 +151,26 @@ def test_fold_rejects_bad_arguments(L, fn):
     assert f(FAKE, 1, 8, 0, FAKE, FAKE, None) == -1
     assert f(FAKE, 3, 8, 8, FAKE, FAKE, None) == -1
     assert f(FAKE, 1, 1 << 40, 1 << 40, FAKE, FAKE, None) == -1     # rows * cols overflows
+
+
+def _qgemm(L, **kw):
+    a = dict(X=ctypes.c_void_p(0x10000), xdt=1, M=4, inn=256, q=ctypes.c_void_p(0x20000), sc=FAKE,
+             z=FAKE, out=64, bits=4, group=128, Y=FAKE, ydt=0, stream=None)
+    a.update(kw)
+    return L.awq_qgemm(a["X"], a["xdt"], a["M"], a["inn"], a["q"], a["sc"], a["z"], a["out"],
+                       a["bits"], a["group"], a["Y"], a["ydt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), -1), (dict(q=None), -1), (dict(sc=None), -1), (dict(z=None), -1),
+    (dict(Y=None), -1), (dict(M=0), -1), (dict(inn=0), -1), (dict(out=0), -1),
+    (dict(group=96), -1), (dict(bits=9), -1), (dict(xdt=4), -1), (dict(ydt=2), -1),
+    (dict(xdt=0), -5), (dict(bits=3), -5), (dict(group=256), -5),
+    (dict(X=ctypes.c_void_p(0x10002)), -5), (dict(q=ctypes.c_void_p(0x20004)), -5),
+    (dict(M=65535 * 32 + 1), -5),
+])
+def test_qgemm_rejects_bad_arguments(L, kw, status):
+    assert _qgemm(L, **kw) == status
 
 
 def test_stats_and_s_table_reject_bad_arguments(L):
