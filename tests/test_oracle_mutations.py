@@ -80,6 +80,40 @@ QGEMM_MUTATIONS = [
   "wd[k] = (double)scales[(g * out + n) % (out * ngroups)] *"),
 ]
 
+# Mistakes in the GPTQ oracle (a Python module): run against its own pins.
+GPTQ_SRC = os.path.join(ROOT, "oracle", "gptq_oracle.py")
+GPTQ_MUTATIONS = [
+ ("gptq no division by U_ii", "err = (W[:, i] - wq) / U[i, i]", "err = (W[:, i] - wq)"),
+ ("gptq column of U", "W[:, i + 1:] -= np.outer(err, U[i, i + 1:])",
+  "W[:, i + 1:] -= np.outer(err, U[i + 1:, i])"),
+ ("gptq update sign", "W[:, i + 1:] -= np.outer(err, U[i, i + 1:])",
+  "W[:, i + 1:] += np.outer(err, U[i, i + 1:])"),
+ ("gptq lower factor", "return np.linalg.cholesky(np.linalg.inv(H)).T",
+  "return np.linalg.cholesky(np.linalg.inv(H))"),
+ ("gptq params on original weights", "scale, zero = group_params(W[:, i:i + group], bits, mode)",
+  "scale, zero = group_params(W0[:, i:i + group], bits, mode)"),
+ ("gptq absolute damping", "H[np.diag_indices_from(H)] += damp * np.mean(np.diag(H))",
+  "H[np.diag_indices_from(H)] += damp"),
+ ("gptq zero sign", "zero = np.round(-lo / scale)", "zero = np.round(lo / scale)"),
+]
+
+
+@pytest.mark.parametrize("name,before,after", GPTQ_MUTATIONS, ids=[m[0] for m in GPTQ_MUTATIONS])
+def test_planted_gptq_mistake_is_caught(tmp_path, name, before, after):
+    src = open(GPTQ_SRC).read()
+    assert before in src, f"pattern for '{name}' no longer in the GPTQ oracle"
+    mutated = src.replace(before, after, 1)
+    if "W0[" in after:
+        mutated = mutated.replace("    W = np.array(W, np.float64)\n",
+                                  "    W = np.array(W, np.float64)\n    W0 = W.copy()\n", 1)
+    path = tmp_path / "gptq_oracle.py"
+    path.write_text(mutated)
+    env = dict(os.environ, AWQ_GPTQ_ORACLE=str(path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_gptq_pins.py")],
+                       env=env, capture_output=True, text=True, cwd=ROOT, timeout=600)
+    assert r.returncode != 0, f"planted mistake '{name}' passed every pin:\n{r.stdout[-500:]}"
+
 
 CASES = ([(n, b, a, "test_oracle_pins.py") for n, b, a in MUTATIONS] +
          [(n, b, a, "test_oracle_clip_pins.py") for n, b, a in CLIP_MUTATIONS] +
