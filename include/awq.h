@@ -249,6 +249,49 @@ int awq_qgemm(const void *X, int x_dtype, int64_t M, int64_t in, const uint32_t 
               const float *scales, const uint8_t *zeros, int64_t out, int bits, int group,
               void *Y, int y_dtype, void *stream);
 
+/* GPTQ on the same layer inputs, a second quantizer producing the same packed
+ * outputs ("AWQ vs GPTQ Quantization Architectures Compared", "GPTQ:
+ * compensate the error you just made"; "Advanced Quantization Algorithms: AWQ
+ * and GPTQ Explained", section 3). In fp64:
+ *   H = 2 X^T X;  H[i][i] += damp * mean(diag H);  U = upper Cholesky factor of H^-1;
+ *   for each column i in order (all rows at once): at a group start fit the
+ *   group's scale (and zero) on the current, already corrected weights of its
+ *   columns; round column i; err = (w_i - dequantized) / U[i][i]; subtract
+ *   err * U[i][j] from every later column j.
+ * The quantizer is awq_quantize_pack's (symmetric or asymmetric), with the
+ * range and scale in fp64 and the scale rounded once to fp32 and used as
+ * stored; divisions and rounding (half to even) in fp64. Columns are processed
+ * in their natural order (no act-order: the packed format has no group index).
+ *   awq_gptq_hessian:  H (device fp64, in x in) = 2 X^T X, damped (damp >= 0, e.g. 0.01).
+ *   awq_gptq_factor:   U (device fp64, in x in, upper; the strict lower part is 0)
+ *                      from H (left unchanged). ws: awq_gptq_factor_workspace_size(in) bytes.
+ *   awq_gptq_quantize: the column loop on W with U; writes qweight, scales and
+ *                      zeros in awq_quantize_pack's layout. ws:
+ *                      awq_gptq_quantize_workspace_size(out, in) bytes.
+ *   awq_gptq:          the three in order with one workspace of
+ *                      awq_gptq_workspace_size(out, in) bytes.
+ * W, X: device (out, in) and (tokens, in) of `dtype`. in must be a multiple of
+ * 128 (the column block); group in {32, 64, 128}; bits 2..8. H is positive
+ * definite for damp > 0 unless a column of X is entirely zero and damp is 0;
+ * otherwise the factor and all outputs are NaN (no error is reported).
+ * The GPU accumulates in a different order from a sequential evaluation, so a
+ * code can differ where a weight lies within about 1e-12 of a rounding
+ * boundary (and the rest of that row may then follow a different path).
+ * AWQ_ERR_UNSUPPORTED: in not a multiple of 128, group not in {32, 64, 128},
+ * out above 4 194 240. */
+int awq_gptq_hessian(const void *X, int dtype, int64_t tokens, int64_t in, double damp, double *H,
+                     void *stream);
+int awq_gptq_factor(const double *H, int64_t in, double *U, void *ws, size_t ws_bytes, void *stream);
+int awq_gptq_quantize(const void *W, int dtype, int64_t out, int64_t in, const double *U, int bits,
+                      int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros, void *ws,
+                      size_t ws_bytes, void *stream);
+int awq_gptq(const void *W, const void *X, int dtype, int64_t out, int64_t in, int64_t tokens, int bits,
+             int group, int mode, double damp, uint32_t *qweight, float *scales, uint8_t *zeros,
+             void *ws, size_t ws_bytes, void *stream);
+size_t awq_gptq_factor_workspace_size(int64_t in);
+size_t awq_gptq_quantize_workspace_size(int64_t out, int64_t in);
+size_t awq_gptq_workspace_size(int64_t out, int64_t in);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *awq_status_string(int status);
 

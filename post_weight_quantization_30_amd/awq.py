@@ -73,6 +73,21 @@ def lib():
         L.awq_scale_cols.restype = cint
         L.awq_qgemm.argtypes = [vp, cint, i64, i64, vp, vp, vp, i64, cint, cint, vp, cint, vp]
         L.awq_qgemm.restype = cint
+        dbl = ctypes.c_double
+        L.awq_gptq_hessian.argtypes = [vp, cint, i64, i64, dbl, vp, vp]
+        L.awq_gptq_hessian.restype = cint
+        L.awq_gptq_factor.argtypes = [vp, i64, vp, vp, sz, vp]
+        L.awq_gptq_factor.restype = cint
+        L.awq_gptq_quantize.argtypes = [vp, cint, i64, i64, vp, cint, cint, cint, vp, vp, vp, vp, sz, vp]
+        L.awq_gptq_quantize.restype = cint
+        L.awq_gptq.argtypes = [vp, vp, cint, i64, i64, i64, cint, cint, cint, dbl, vp, vp, vp, vp, sz, vp]
+        L.awq_gptq.restype = cint
+        for fn in ("awq_gptq_factor_workspace_size",):
+            getattr(L, fn).argtypes = [i64]
+            getattr(L, fn).restype = sz
+        for fn in ("awq_gptq_quantize_workspace_size", "awq_gptq_workspace_size"):
+            getattr(L, fn).argtypes = [i64, i64]
+            getattr(L, fn).restype = sz
         L.awq_status_string.argtypes = [cint]
         L.awq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -290,6 +305,58 @@ def qgemm(X, qweight, scales, zeros, bits, group, y=None, y_f32=False):
         _dev(scales, "scales", torch.float32), _dev(zeros, "zeros", torch.uint8), out, bits, group,
         _dev(y, "y", ydt), _DTYPE[ydt], _stream()))
     return y
+
+
+def _packed_outputs(out, n_in, bits, group, dev):
+    return (torch.empty((out, words_per_row(n_in, bits)), dtype=torch.int32, device=dev),
+            torch.empty((out, n_in // group), dtype=torch.float32, device=dev),
+            torch.empty((out, n_in // group), dtype=torch.uint8, device=dev))
+
+
+def gptq_hessian(X, damp=0.01, H=None):
+    """H (in, in) fp64 = 2 X^T X plus damp * mean(diag) on the diagonal."""
+    T, n_in = X.shape
+    H = torch.empty((n_in, n_in), dtype=torch.float64, device=X.device) if H is None else H
+    _check("awq_gptq_hessian", lib().awq_gptq_hessian(
+        _dev(X, "X"), _dtype_code(X), T, n_in, float(damp), _dev(H, "H", torch.float64), _stream()))
+    return H
+
+
+def gptq_factor(H, U=None, workspace=None):
+    """U (in, in) fp64, upper, with H^-1 = U^T U."""
+    n_in = H.shape[0]
+    U = torch.empty_like(H) if U is None else U
+    ws = _workspace(int(lib().awq_gptq_factor_workspace_size(n_in)), H.device, workspace)
+    _check("awq_gptq_factor", lib().awq_gptq_factor(
+        _dev(H, "H", torch.float64), n_in, _dev(U, "U", torch.float64), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream()))
+    return U
+
+
+def gptq_quantize(W, U, bits, group, mode, workspace=None):
+    """The column loop on W with U; returns (qweight, scales, zeros)."""
+    out, n_in = W.shape
+    q, sc, z = _packed_outputs(out, n_in, bits, group, W.device)
+    ws = _workspace(int(lib().awq_gptq_quantize_workspace_size(out, n_in)), W.device, workspace)
+    _check("awq_gptq_quantize", lib().awq_gptq_quantize(
+        _dev(W, "W"), _dtype_code(W), out, n_in, _dev(U, "U", torch.float64), bits, group, _MODE[mode],
+        _dev(q, "qweight"), _dev(sc, "scales", torch.float32), _dev(z, "zeros", torch.uint8),
+        _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()))
+    return q, sc, z
+
+
+def gptq(W, X, bits=4, group=128, mode="asym", damp=0.01, workspace=None):
+    """GPTQ of one layer; returns (qweight, scales, zeros) in the packed layout."""
+    out, n_in = W.shape
+    if X.shape[1] != n_in or X.dtype != W.dtype:
+        raise ValueError("W (out, in) and X (tokens, in) must share in and dtype")
+    q, sc, z = _packed_outputs(out, n_in, bits, group, W.device)
+    ws = _workspace(int(lib().awq_gptq_workspace_size(out, n_in)), W.device, workspace)
+    _check("awq_gptq", lib().awq_gptq(
+        _dev(W, "W"), _dev(X, "X"), _dtype_code(W), out, n_in, X.shape[0], bits, group, _MODE[mode],
+        float(damp), _dev(q, "qweight"), _dev(sc, "scales", torch.float32), _dev(z, "zeros", torch.uint8),
+        _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()))
+    return q, sc, z
 
 
 def quantize_layer(W, X, bits=4, group=128, grid=20, mode="sym", n_clip=0, max_shrink=0.5):

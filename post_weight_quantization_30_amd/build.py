@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libawq.so")
-SOURCES = ["abi.hip", "k_stats.hip", "k_search.hip", "k_pack.hip", "k_clip.hip", "k_fold.hip", "k_qgemm.hip"]
+SOURCES = ["abi.hip", "k_stats.hip", "k_search.hip", "k_pack.hip", "k_clip.hip", "k_fold.hip", "k_qgemm.hip", "k_gptq.hip"]
 # Standalone measurement program: the attainable MFMA peak (bench.py runs it).
 PROBE_SRC = "mfma_peak.hip"
 PROBE = os.path.join(PKG, "mfma_peak")

@@ -221,6 +221,111 @@ int awq_scale_cols(const void *W, int dtype, int64_t rows, int64_t cols, const f
     return fold_call(W, dtype, rows, cols, s, out, true, stream);
 }
 
+size_t awq_gptq_factor_workspace_size(int64_t in)
+{
+    if (in < 1)
+        return 0;
+    return awq::align256((size_t)(in * in + 64 * in) * sizeof(double));
+}
+
+size_t awq_gptq_quantize_workspace_size(int64_t out, int64_t in)
+{
+    if (out < 1 || in < 1)
+        return 0;
+    return awq::align256((size_t)(out * in + out * 128) * sizeof(double));
+}
+
+size_t awq_gptq_workspace_size(int64_t out, int64_t in)
+{
+    if (out < 1 || in < 1)
+        return 0;
+    const size_t f = awq_gptq_factor_workspace_size(in), q = awq_gptq_quantize_workspace_size(out, in);
+    return 2 * awq::align256((size_t)(in * in) * sizeof(double)) + (f > q ? f : q);
+}
+
+namespace {
+
+int gptq_shape(int64_t in)
+{
+    if (in < 1)
+        return AWQ_ERR_INVALID_ARG;
+    if (in % 128 != 0 || in > 65535LL * 64)
+        return AWQ_ERR_UNSUPPORTED;
+    return AWQ_OK;
+}
+
+}  // namespace
+
+int awq_gptq_hessian(const void *X, int dtype, int64_t tokens, int64_t in, double damp, double *H,
+                     void *stream)
+{
+    if (!X || !H || tokens < 1 || !valid_dtype(dtype) || !(damp >= 0.0 && damp < 1e300))
+        return AWQ_ERR_INVALID_ARG;
+    int st = gptq_shape(in);
+    if (st != AWQ_OK)
+        return st;
+    return hip_status(awq::launch_gptq_hessian(X, dtype, tokens, in, damp, H, (hipStream_t)stream));
+}
+
+int awq_gptq_factor(const double *H, int64_t in, double *U, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!H || !U)
+        return AWQ_ERR_INVALID_ARG;
+    int st = gptq_shape(in);
+    if (st != AWQ_OK)
+        return st;
+    if (!ws || ws_bytes < awq_gptq_factor_workspace_size(in))
+        return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_gptq_factor(H, in, U, (double *)ws, (hipStream_t)stream));
+}
+
+int awq_gptq_quantize(const void *W, int dtype, int64_t out, int64_t in, const double *U, int bits,
+                      int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros, void *ws,
+                      size_t ws_bytes, void *stream)
+{
+    if (!W || !U || !qweight || !scales || !zeros || out < 1 || group < 1 || in % group != 0 ||
+        bits < 2 || bits > 8 || !valid_dtype(dtype) || !valid_mode(mode))
+        return AWQ_ERR_INVALID_ARG;
+    int st = gptq_shape(in);
+    if (st != AWQ_OK)
+        return st;
+    if (!search_group_ok(group) || (out + 3) / 4 > (int64_t)0x7fffffff || out > 65535LL * 64)
+        return AWQ_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < awq_gptq_quantize_workspace_size(out, in))
+        return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_gptq_quantize(W, dtype, out, in, U, bits, group, mode, qweight, scales,
+                                                zeros, (double *)ws, (hipStream_t)stream));
+}
+
+int awq_gptq(const void *W, const void *X, int dtype, int64_t out, int64_t in, int64_t tokens, int bits,
+             int group, int mode, double damp, uint32_t *qweight, float *scales, uint8_t *zeros,
+             void *ws, size_t ws_bytes, void *stream)
+{
+    if (!W || !X || !qweight || !scales || !zeros || out < 1 || tokens < 1 || group < 1 || in < 1 ||
+        in % group != 0 || bits < 2 || bits > 8 || !valid_dtype(dtype) || !valid_mode(mode) ||
+        !(damp >= 0.0 && damp < 1e300))
+        return AWQ_ERR_INVALID_ARG;
+    int st = gptq_shape(in);
+    if (st != AWQ_OK)
+        return st;
+    if (!search_group_ok(group) || out > 65535LL * 64)
+        return AWQ_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < awq_gptq_workspace_size(out, in))
+        return AWQ_ERR_WORKSPACE;
+    char *base = (char *)ws;
+    const size_t hb = awq::align256((size_t)(in * in) * sizeof(double));
+    double *H = (double *)base, *U = (double *)(base + hb);
+    void *rest = base + 2 * hb;
+    const size_t rest_bytes = ws_bytes - 2 * hb;
+    st = awq_gptq_hessian(X, dtype, tokens, in, damp, H, stream);
+    if (st == AWQ_OK)
+        st = awq_gptq_factor(H, in, U, rest, rest_bytes, stream);
+    if (st == AWQ_OK)
+        st = awq_gptq_quantize(W, dtype, out, in, U, bits, group, mode, qweight, scales, zeros, rest,
+                               rest_bytes, stream);
+    return st;
+}
+
 int awq_qgemm(const void *X, int x_dtype, int64_t M, int64_t in, const uint32_t *qweight,
               const float *scales, const uint8_t *zeros, int64_t out, int bits, int group, void *Y,
               int y_dtype, void *stream)

@@ -85,6 +85,12 @@ hipError_t launch_reduce_argmin(const double *partial, int64_t nblk, int n_alpha
 hipError_t launch_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s,
                        const float *clip, int bits, int group, int mode, uint32_t *qweight,
                        float *scales, uint8_t *zeros, hipStream_t st);
+hipError_t launch_gptq_hessian(const void *X, int dtype, int64_t tokens, int64_t in, double damp, double *H,
+                               hipStream_t st);
+hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws, hipStream_t st);
+hipError_t launch_gptq_quantize(const void *W, int dtype, int64_t out, int64_t in, const double *U, int bits,
+                                int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros,
+                                double *ws, hipStream_t st);
 hipError_t launch_qgemm(const void *X, int dtype, int64_t M, int64_t in, const uint32_t *qweight,
                         const float *scales, const uint8_t *zeros, int64_t out, int bits, int group,
                         void *Y, bool yf32, hipStream_t st);

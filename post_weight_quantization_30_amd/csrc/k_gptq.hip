@@ -1,0 +1,473 @@
+// k_gptq.hip -- GPTQ on the same layer inputs, in fp64 on the matrix cores.
+//
+// What is computed ("AWQ vs GPTQ Quantization Architectures Compared", "GPTQ:
+// compensate the error you just made"; "Advanced Quantization Algorithms: AWQ
+// and GPTQ Explained", section 3): H = 2 X^T X plus damp * mean(diag H) on the
+// diagonal; U = the upper Cholesky factor of H^-1 (H^-1 = U^T U); then, column
+// by column for all rows at once, group parameters fitted on the already
+// corrected weights at each group start, the column rounded, and its error
+// divided by U[i][i] and pushed into the later columns along row i of U.
+// Everything is fp64, the precision of the pages' listing, so that the integer
+// codes follow the same decisions.
+//
+// How:
+//  - one fp64 MFMA GEMM kernel (v_mfma_f64_16x16x4f64, 64 x 64 tiles staged
+//    through LDS) serves the Hessian, the Cholesky trailing updates, the
+//    triangular-inverse products and GPTQ's lazy block updates;
+//  - U without forming H^-1: with J the index reversal, the lower Cholesky
+//    factor L of J H J gives H = (J L J)(J L J)^T with J L J upper, hence
+//    H^-1 = (J L^-1 J)^T (J L^-1 J) and, by uniqueness, U = J L^-1 J: one
+//    blocked Cholesky and one blocked triangular inverse (panels of 64);
+//  - the column loop in blocks of 128 columns: one wave per row takes the
+//    block's columns one at a time (lanes own two columns each; the column's
+//    value is broadcast, the quantizer runs uniformly, every lane updates its
+//    later columns), then one GEMM applies the block's 128 errors to all later
+//    columns (the page's "batch the updates in blocks of 128").
+#include "awq_internal.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace awq {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNb = 64;          // Cholesky / inverse panel
+constexpr int kCol = 128;        // GPTQ column block
+
+// ---------------------------------------------------------------------------
+// C[m][n] = alpha * sum_k A(m, k) B(k, n) + beta * C[m][n]
+// A(m, k) = TA ? A[k lda + m] : A[m lda + k];  B(k, n) = TB ? B[n ldb + k] : B[k ldb + n].
+// LOWER: tiles entirely above the diagonal are skipped (only the lower
+// triangle of C is wanted). Block: 64 x 64 of C, 4 waves of 32 x 32; k in
+// steps of 16 through LDS (padded rows); out-of-range elements load as 0.
+// ---------------------------------------------------------------------------
+template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER>
+__global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha,
+                                               const TAe *__restrict__ A, int64_t lda,
+                                               const TBe *__restrict__ B, int64_t ldb, double beta,
+                                               double *__restrict__ C, int64_t ldc)
+{
+    __shared__ double As[16][65];
+    __shared__ double Bs[16][65];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    if (LOWER && n0 > m0 + 63)
+        return;                                    // uniform for the block, before any barrier
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int64_t k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+        for (int e0 = 0; e0 < 1024; e0 += 256) {
+            const int e = e0 + tid;
+            int mm, kk;
+            if (TA) { mm = e & 63; kk = e >> 6; } else { kk = e & 15; mm = e >> 4; }
+            const int64_t m = m0 + mm, k = k0 + kk;
+            double v = 0.0;
+            if (m < M && k < K)
+                v = static_cast<double>(TA ? A[k * lda + m] : A[m * lda + k]);
+            As[kk][mm] = v;
+            int nn;
+            if (TB) { kk = e & 15; nn = e >> 4; } else { nn = e & 63; kk = e >> 6; }
+            const int64_t n = n0 + nn, k2 = k0 + kk;
+            double u = 0.0;
+            if (n < N && k2 < K)
+                u = static_cast<double>(TB ? B[n * ldb + k2] : B[k2 * ldb + n]);
+            Bs[kk][nn] = u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const double a = As[kk + (lane >> 4)][wm + i * 16 + (lane & 15)];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const double b = Bs[kk + (lane >> 4)][wn + j * 16 + (lane & 15)];
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // v_mfma_f64_16x16x4f64: element r of lane l is D[l / 16 + 4 r][l % 16]
+                const int64_t m = m0 + wm + i * 16 + (lane >> 4) + 4 * r;
+                const int64_t n = n0 + wn + j * 16 + (lane & 15);
+                if (m < M && n < N) {
+                    double *c = C + m * ldc + n;
+                    const double prod = alpha * acc[i][j][r];
+                    *c = beta == 0.0 ? prod : fma(beta, *c, prod);
+                }
+            }
+}
+
+template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER>
+static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, int64_t lda, const TBe *B,
+                  int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st)
+{
+    if (M <= 0 || N <= 0)
+        return;
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER>), grid, dim3(256), 0, st, M, N, K, alpha, A, lda,
+                       B, ldb, beta, C, ldc);
+}
+
+// ---------------------------------------------------------------------------
+// Dampening: H[i][i] += damp * mean(diag H). One block; fixed summation order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_damp(double *H, int64_t n, double damp)
+{
+    __shared__ double part[256];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 256)
+        s += H[i * n + i];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w)
+            part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    const double add = damp * (part[0] / (double)n);
+    for (int64_t i = threadIdx.x; i < n; i += 256)
+        H[i * n + i] += add;
+}
+
+// Reversing both indices of an n x n matrix, (i, j) -> (n-1-i, n-1-j), is
+// reversing its flattened array: e -> n*n - 1 - e.
+__global__ __launch_bounds__(256) void k_reverse_copy(const double *__restrict__ src, double *__restrict__ dst,
+                                                      int64_t total)
+{
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
+        dst[e] = src[total - 1 - e];
+}
+
+__global__ __launch_bounds__(256) void k_reverse_inplace(double *a, int64_t total)
+{
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total / 2; e += (int64_t)gridDim.x * 256) {
+        const double x = a[e];
+        a[e] = a[total - 1 - e];
+        a[total - 1 - e] = x;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fill0(double *a, int64_t total)
+{
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
+        a[e] = 0.0;
+}
+
+// ---------------------------------------------------------------------------
+// Cholesky of the 64 x 64 diagonal block at (k0, k0), in place (lower): the
+// trailing updates of earlier panels are already applied.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_potrf_diag(double *A, int64_t n, int64_t k0)
+{
+    __shared__ double a[kNb][kNb + 1];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < kNb * kNb; e += 256)
+        a[e / kNb][e % kNb] = A[(k0 + e / kNb) * n + k0 + e % kNb];
+    __syncthreads();
+    for (int j = 0; j < kNb; ++j) {
+        if (tid == 0)
+            a[j][j] = sqrt(a[j][j]);
+        __syncthreads();
+        if (tid > j && tid < kNb)
+            a[tid][j] /= a[j][j];
+        __syncthreads();
+        // trailing update of the block: a[i][l] -= a[i][j] a[l][j], j < l <= i
+        for (int e = tid; e < kNb * kNb; e += 256) {
+            const int i = e / kNb, l = e % kNb;
+            if (l > j && i >= l)
+                a[i][l] -= a[i][j] * a[l][j];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < kNb * kNb; e += 256) {
+        const int i = e / kNb, l = e % kNb;
+        if (l <= i)
+            A[(k0 + i) * n + k0 + l] = a[i][l];
+    }
+}
+
+// Rows below the diagonal block: A[r][k0..k0+63] <- A[r][k0..] L_kk^-T
+// (forward substitution along the row), one row per thread, L_kk in LDS.
+__global__ __launch_bounds__(64) void k_trsm_panel(double *A, int64_t n, int64_t k0)
+{
+    __shared__ double l[kNb][kNb + 1];
+    for (int e = threadIdx.x; e < kNb * kNb; e += 64)
+        l[e / kNb][e % kNb] = A[(k0 + e / kNb) * n + k0 + e % kNb];
+    __syncthreads();
+    const int64_t r = k0 + kNb + (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (r >= n)
+        return;
+    double x[kNb];
+    double *row = A + r * n + k0;
+#pragma unroll
+    for (int j = 0; j < kNb; ++j)
+        x[j] = row[j];
+#pragma unroll
+    for (int j = 0; j < kNb; ++j) {
+        double s = x[j];
+#pragma unroll
+        for (int q = 0; q < j; ++q)
+            s -= x[q] * l[j][q];
+        x[j] = s / l[j][j];
+    }
+#pragma unroll
+    for (int j = 0; j < kNb; ++j)
+        row[j] = x[j];
+}
+
+// Inverse of every 64 x 64 diagonal block of the lower triangular L (one block
+// each; column j of the inverse by forward substitution, one thread per column).
+__global__ __launch_bounds__(64) void k_trtri_diag(const double *L, double *Li, int64_t n)
+{
+    __shared__ double l[kNb][kNb + 1];
+    const int64_t k0 = (int64_t)blockIdx.x * kNb;
+    for (int e = threadIdx.x; e < kNb * kNb; e += 64)
+        l[e / kNb][e % kNb] = L[(k0 + e / kNb) * n + k0 + e % kNb];
+    __syncthreads();
+    const int j = threadIdx.x;
+    double x[kNb];
+#pragma unroll
+    for (int i = 0; i < kNb; ++i) {
+        double s = i == j ? 1.0 : 0.0;
+#pragma unroll
+        for (int q = 0; q < i; ++q)
+            s -= l[i][q] * x[q];
+        x[i] = i < j ? 0.0 : s / l[i][i];
+    }
+#pragma unroll
+    for (int i = 0; i < kNb; ++i)
+        Li[(k0 + i) * n + k0 + j] = x[i];
+}
+
+// ---------------------------------------------------------------------------
+// One block of 128 columns [b, b + 128) for one row per wave. Lane l owns the
+// row's columns b + l and b + 64 + l.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double bcast(double v, int src)
+{
+    const long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffffLL), src);
+    const int hi = __builtin_amdgcn_readlane((int)(u >> 32), src);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double wave_max(double v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmax(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ double wave_min(double v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmin(v, __shfl_xor(v, off));
+    return v;
+}
+
+__global__ __launch_bounds__(256) void k_gptq_block(double *__restrict__ Wc, const double *__restrict__ U,
+                                                    int64_t out, int64_t in, int64_t b, int bits, int group,
+                                                    int mode, double *__restrict__ E,
+                                                    uint32_t *__restrict__ qweight, float *__restrict__ scales,
+                                                    uint8_t *__restrict__ zeros)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t o = (int64_t)blockIdx.x * 4 + wv;
+    if (o >= out)
+        return;                                    // whole wave; no block-level barrier below
+    double *row = Wc + o * in + b;
+    double w0 = row[lane], w1 = row[64 + lane];
+    double e0 = 0.0, e1 = 0.0;
+    uint32_t c0 = 0, c1 = 0;
+    const double maxq = (double)((1 << bits) - 1);
+    const double L = (double)((1 << (bits - 1)) - 1);
+    const int64_t ng = in / group;
+    double scale = 1.0, zero = 0.0;
+    for (int jj = 0; jj < kCol; ++jj) {
+        const int64_t j = b + jj;
+        if (jj % group == 0) {
+            // group parameters on the current (corrected) weights of [j, j + group)
+            const bool in0 = lane >= jj && lane < jj + group;
+            const bool in1 = 64 + lane >= jj && 64 + lane < jj + group;
+            double s64;
+            if (mode == AWQ_ASYM) {
+                double lo = 0.0, hi = 0.0;     // the range always contains 0
+                if (in0) { lo = fmin(lo, w0); hi = fmax(hi, w0); }
+                if (in1) { lo = fmin(lo, w1); hi = fmax(hi, w1); }
+                lo = wave_min(lo);
+                hi = wave_max(hi);
+                s64 = fmax((hi - lo) / maxq, 1e-8);
+                scale = (double)(float)s64;
+                zero = rint(-lo / scale);
+            } else {
+                double a = 0.0;
+                if (in0) a = fmax(a, fabs(w0));
+                if (in1) a = fmax(a, fabs(w1));
+                a = wave_max(a);
+                s64 = fmax(a / L, 1e-8);
+                scale = (double)(float)s64;
+                zero = (double)(1 << (bits - 1));
+            }
+            if (lane == 0) {
+                scales[o * ng + j / group] = (float)scale;
+                zeros[o * ng + j / group] = (uint8_t)(int)zero;
+            }
+        }
+        const int owner = jj & 63;
+        const double w = bcast(jj < 64 ? w0 : w1, owner);
+        double q, wq;
+        uint32_t code;
+        if (mode == AWQ_ASYM) {
+            q = fmin(fmax(rint(w / scale) + zero, 0.0), maxq);
+            wq = scale * (q - zero);
+            code = (uint32_t)(int)q;
+        } else {
+            q = fmin(fmax(rint(w / scale), -L - 1.0), L);
+            wq = scale * q;
+            code = (uint32_t)((int)q + (1 << (bits - 1)));
+        }
+        const double err = (w - wq) / U[j * in + j];
+        if (lane == owner) {
+            if (jj < 64) { e0 = err; c0 = code; } else { e1 = err; c1 = code; }
+        }
+        const double *urow = U + j * in + b;
+        if (lane > jj)
+            w0 -= err * urow[lane];
+        if (64 + lane > jj)
+            w1 -= err * urow[64 + lane];
+    }
+    E[o * kCol + lane] = e0;
+    E[o * kCol + 64 + lane] = e1;
+    // the block's 128 codes fill exactly 4 * bits words of the row's stream:
+    // every code is broadcast in turn and each of the first 4 * bits lanes
+    // keeps the bits that fall into its word
+    uint32_t word = 0;
+    for (int i = 0; i < kCol; ++i) {
+        const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)(i < 64 ? c0 : c1), i & 63);
+        const int sh = i * bits - 32 * lane;
+        if (sh >= 0 && sh < 32)
+            word |= c << sh;
+        else if (sh < 0 && sh > -bits)
+            word |= c >> -sh;
+    }
+    if (lane < 4 * bits) {
+        const int64_t wpr = in * bits / 32;
+        qweight[o * wpr + (b * bits) / 32 + lane] = word;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <typename T>
+static void hessian_typed(const T *X, int64_t tokens, int64_t in, double *H, hipStream_t st)
+{
+    // H = 2 X^T X: A(m, k) = X[k][m] (TA), B(k, n) = X[k][n]
+    dgemm<T, T, true, false, false>(in, in, tokens, 2.0, X, in, X, in, 0.0, H, in, st);
+}
+
+hipError_t launch_gptq_hessian(const void *X, int dtype, int64_t tokens, int64_t in, double damp, double *H,
+                               hipStream_t st)
+{
+    switch (dtype) {
+    case AWQ_F32: hessian_typed((const float *)X, tokens, in, H, st); break;
+    case AWQ_F16: hessian_typed((const f16 *)X, tokens, in, H, st); break;
+    default: hessian_typed((const bf16 *)X, tokens, in, H, st); break;
+    }
+    hipLaunchKernelGGL(k_damp, dim3(1), dim3(256), 0, st, H, in, damp);
+    return hipGetLastError();
+}
+
+static unsigned stream_blocks(int64_t total)
+{
+    const int64_t b = (total + 255) / 256;
+    return (unsigned)(b < 65536 ? (b > 0 ? b : 1) : 65536);
+}
+
+// U = J L^-1 J, L the lower Cholesky factor of J H J. ws: n*n + 64*n doubles.
+hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws, hipStream_t st)
+{
+    const int64_t total = n * n;
+    double *Lr = ws;                       // J H J, then (lower part) its Cholesky factor
+    double *T = ws + total;                // 64 x n bracket of the inverse recurrence
+    hipLaunchKernelGGL(k_reverse_copy, dim3(stream_blocks(total)), dim3(256), 0, st, H, Lr, total);
+    const int64_t nb = n / kNb;
+    for (int64_t k = 0; k < nb; ++k) {
+        const int64_t k0 = k * kNb, rest = n - k0 - kNb;
+        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, st, Lr, n, k0);
+        if (rest > 0) {
+            hipLaunchKernelGGL(k_trsm_panel, dim3((unsigned)((rest + 63) / 64)), dim3(64), 0, st, Lr, n, k0);
+            // trailing lower triangle -= P P^T, P = the panel below the diagonal block
+            const double *P = Lr + (k0 + kNb) * n + k0;
+            dgemm<double, double, false, true, true>(rest, rest, kNb, -1.0, P, n, P, n, 1.0,
+                                                     Lr + (k0 + kNb) * n + k0 + kNb, n, st);
+        }
+    }
+    // Li = L^-1 in U's buffer: zero, invert the diagonal blocks, then block row
+    // by block row Li[I][:I] = -Li[I][I] (L[I][:I] Li[:I][:I]).
+    double *Li = U;
+    hipLaunchKernelGGL(k_fill0, dim3(stream_blocks(total)), dim3(256), 0, st, Li, total);
+    hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, Lr, Li, n);
+    for (int64_t I = 1; I < nb; ++I) {
+        const int64_t r0 = I * kNb;
+        dgemm<double, double, false, false, false>(kNb, r0, r0, 1.0, Lr + r0 * n, n, Li, n, 0.0, T, n, st);
+        dgemm<double, double, false, false, false>(kNb, r0, kNb, -1.0, Li + r0 * n + r0, n, T, n, 0.0,
+                                                   Li + r0 * n, n, st);
+    }
+    hipLaunchKernelGGL(k_reverse_inplace, dim3(stream_blocks(total / 2)), dim3(256), 0, st, U, total);
+    return hipGetLastError();
+}
+
+// The column loop. ws: out*in (corrected weights) + out*128 (block errors) doubles.
+template <typename T>
+__global__ __launch_bounds__(256) void k_widen(const T *__restrict__ W, double *__restrict__ Wc, int64_t total)
+{
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
+        Wc[e] = static_cast<double>(static_cast<float>(W[e]));
+}
+
+hipError_t launch_gptq_quantize(const void *W, int dtype, int64_t out, int64_t in, const double *U, int bits,
+                                int group, int mode, uint32_t *qweight, float *scales, uint8_t *zeros,
+                                double *ws, hipStream_t st)
+{
+    double *Wc = ws;
+    double *E = ws + out * in;
+    const int64_t total = out * in;
+    switch (dtype) {
+    case AWQ_F32:
+        hipLaunchKernelGGL(k_widen<float>, dim3(stream_blocks(total)), dim3(256), 0, st, (const float *)W, Wc, total);
+        break;
+    case AWQ_F16:
+        hipLaunchKernelGGL(k_widen<f16>, dim3(stream_blocks(total)), dim3(256), 0, st, (const f16 *)W, Wc, total);
+        break;
+    default:
+        hipLaunchKernelGGL(k_widen<bf16>, dim3(stream_blocks(total)), dim3(256), 0, st, (const bf16 *)W, Wc, total);
+        break;
+    }
+    for (int64_t b = 0; b < in; b += kCol) {
+        hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)((out + 3) / 4)), dim3(256), 0, st, Wc, U, out, in, b,
+                           bits, group, mode, E, qweight, scales, zeros);
+        const int64_t rest = in - b - kCol;
+        if (rest > 0)   // later columns -= E U[b : b + 128][b + 128 :]
+            dgemm<double, double, false, false, false>(out, rest, kCol, -1.0, E, kCol, U + b * in + b + kCol, in,
+                                                       1.0, Wc + b + kCol, in, st);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace awq

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search", "awq_quantize_pack", "awq_s_table",
-              "awq_clip_search", "awq_quantize_pack_clip", "awq_fold_rows", "awq_scale_cols", "awq_qgemm",
+              "awq_clip_search", "awq_quantize_pack_clip", "awq_fold_rows", "awq_scale_cols", "awq_qgemm", "awq_gptq",
+              "awq_gptq_hessian", "awq_gptq_factor", "awq_gptq_quantize", "awq_gptq_workspace_size",
               "awq_act_stats_workspace_size", "awq_search_workspace_size", "awq_status_string"):
         assert n in names
 
@@ -171,6 +172,27 @@ def _qgemm(L, **kw):
 ])
 def test_qgemm_rejects_bad_arguments(L, kw, status):
     assert _qgemm(L, **kw) == status
+
+
+def test_gptq_rejects_bad_arguments(L):
+    d = ctypes.c_double
+    assert L.awq_gptq_hessian(None, 1, 8, 128, d(0.01), FAKE, None) == -1
+    assert L.awq_gptq_hessian(FAKE, 1, 0, 128, d(0.01), FAKE, None) == -1
+    assert L.awq_gptq_hessian(FAKE, 1, 8, 128, d(-1.0), FAKE, None) == -1
+    assert L.awq_gptq_hessian(FAKE, 1, 8, 100, d(0.01), FAKE, None) == -5      # in % 128
+    assert L.awq_gptq_factor(FAKE, 128, FAKE, FAKE, 16, None) == -2
+    assert L.awq_gptq_factor(FAKE, 96, FAKE, FAKE, BIG, None) == -5
+    args = dict(W=FAKE, dt=1, out=8, inn=256, U=FAKE, bits=4, group=128, mode=0, q=FAKE, s=FAKE, z=FAKE,
+                ws=FAKE, wsb=BIG)
+    def quant(**kw):
+        a = dict(args); a.update(kw)
+        return L.awq_gptq_quantize(a["W"], a["dt"], a["out"], a["inn"], a["U"], a["bits"], a["group"],
+                                   a["mode"], a["q"], a["s"], a["z"], a["ws"], a["wsb"], None)
+    assert quant(W=None) == -1 and quant(bits=9) == -1 and quant(group=96) == -1 and quant(mode=3) == -1
+    assert quant(group=256) == -5 and quant(wsb=8) == -2
+    assert L.awq_gptq_quantize_workspace_size(8, 256) >= (8 * 256 + 8 * 128) * 8
+    assert L.awq_gptq_workspace_size(4096, 4096) >= 8 * (3 * 4096 * 4096 + 4096 * 128)
+    assert L.awq_gptq(FAKE, FAKE, 1, 8, 256, 16, 4, 128, 0, d(0.01), FAKE, FAKE, FAKE, FAKE, 8, None) == -2
 
 
 def test_stats_and_s_table_reject_bad_arguments(L):
