@@ -225,7 +225,7 @@ size_t awq_gptq_factor_workspace_size(int64_t in)
 {
     if (in < 1)
         return 0;
-    return awq::align256((size_t)(in * in + 64 * in) * sizeof(double));
+    return awq::align256((size_t)(in * in + (in * in + 3) / 4) * sizeof(double));
 }
 
 size_t awq_gptq_quantize_workspace_size(int64_t out, int64_t in)

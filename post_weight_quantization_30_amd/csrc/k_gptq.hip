@@ -37,17 +37,39 @@ constexpr int kNb = 64;          // Cholesky / inverse panel
 constexpr int kCol = 128;        // GPTQ column block
 
 // ---------------------------------------------------------------------------
-// C[m][n] = alpha * sum_k A(m, k) B(k, n) + beta * C[m][n]
+// C[m][n] = alpha * sum_k A(m, k) B(k, n) + beta * C[m][n], for each batch z
+// (blockIdx.z) with A, B, C advanced by z * sA, z * sB, z * sC.
 // A(m, k) = TA ? A[k lda + m] : A[m lda + k];  B(k, n) = TB ? B[n ldb + k] : B[k ldb + n].
 // LOWER: tiles entirely above the diagonal are skipped (only the lower
 // triangle of C is wanted). Block: 64 x 64 of C, 4 waves of 32 x 32; k in
-// steps of 16 through LDS (padded rows); out-of-range elements load as 0.
+// steps of 16 through LDS (padded rows), the next step's elements loaded into
+// registers while the current one is multiplied; out-of-range elements load
+// as 0.
 // ---------------------------------------------------------------------------
+template <typename TAe, typename TBe, bool TA, bool TB>
+__device__ __forceinline__ void dgemm_fetch(const TAe *A, int64_t lda, const TBe *B, int64_t ldb, int64_t M,
+                                            int64_t N, int64_t K, int64_t m0, int64_t n0, int64_t k0, int tid,
+                                            double (&ra)[4], double (&rb)[4])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = q * 256 + tid;
+        int mm, kk;
+        if (TA) { mm = e & 63; kk = e >> 6; } else { kk = e & 15; mm = e >> 4; }
+        const int64_t m = m0 + mm, k = k0 + kk;
+        ra[q] = (m < M && k < K) ? static_cast<double>(TA ? A[k * lda + m] : A[m * lda + k]) : 0.0;
+        int nn;
+        if (TB) { kk = e & 15; nn = e >> 4; } else { nn = e & 63; kk = e >> 6; }
+        const int64_t n = n0 + nn, k2 = k0 + kk;
+        rb[q] = (n < N && k2 < K) ? static_cast<double>(TB ? B[n * ldb + k2] : B[k2 * ldb + n]) : 0.0;
+    }
+}
+
 template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER>
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha,
-                                               const TAe *__restrict__ A, int64_t lda,
-                                               const TBe *__restrict__ B, int64_t ldb, double beta,
-                                               double *__restrict__ C, int64_t ldc)
+                                               const TAe *__restrict__ A, int64_t lda, int64_t sA,
+                                               const TBe *__restrict__ B, int64_t ldb, int64_t sB, double beta,
+                                               double *__restrict__ C, int64_t ldc, int64_t sC)
 {
     __shared__ double As[16][65];
     __shared__ double Bs[16][65];
@@ -55,6 +77,9 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
     if (LOWER && n0 > m0 + 63)
         return;                                    // uniform for the block, before any barrier
+    A += (int64_t)blockIdx.z * sA;
+    B += (int64_t)blockIdx.z * sB;
+    C += (int64_t)blockIdx.z * sC;
     const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
     f64x4 acc[2][2];
 #pragma unroll
@@ -62,26 +87,18 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double ra[4], rb[4];
+    dgemm_fetch<TAe, TBe, TA, TB>(A, lda, B, ldb, M, N, K, m0, n0, 0, tid, ra, rb);
     for (int64_t k0 = 0; k0 < K; k0 += 16) {
 #pragma unroll
-        for (int e0 = 0; e0 < 1024; e0 += 256) {
-            const int e = e0 + tid;
-            int mm, kk;
-            if (TA) { mm = e & 63; kk = e >> 6; } else { kk = e & 15; mm = e >> 4; }
-            const int64_t m = m0 + mm, k = k0 + kk;
-            double v = 0.0;
-            if (m < M && k < K)
-                v = static_cast<double>(TA ? A[k * lda + m] : A[m * lda + k]);
-            As[kk][mm] = v;
-            int nn;
-            if (TB) { kk = e & 15; nn = e >> 4; } else { nn = e & 63; kk = e >> 6; }
-            const int64_t n = n0 + nn, k2 = k0 + kk;
-            double u = 0.0;
-            if (n < N && k2 < K)
-                u = static_cast<double>(TB ? B[n * ldb + k2] : B[k2 * ldb + n]);
-            Bs[kk][nn] = u;
+        for (int q = 0; q < 4; ++q) {
+            const int e = q * 256 + tid;
+            if (TA) As[e >> 6][e & 63] = ra[q]; else As[e & 15][e >> 4] = ra[q];
+            if (TB) Bs[e & 15][e >> 4] = rb[q]; else Bs[e >> 6][e & 63] = rb[q];
         }
         __syncthreads();
+        if (k0 + 16 < K)
+            dgemm_fetch<TAe, TBe, TA, TB>(A, lda, B, ldb, M, N, K, m0, n0, k0 + 16, tid, ra, rb);
 #pragma unroll
         for (int kk = 0; kk < 16; kk += 4) {
 #pragma unroll
@@ -115,13 +132,14 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
 
 template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER>
 static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, int64_t lda, const TBe *B,
-                  int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st)
+                  int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st, int64_t batch = 1,
+                  int64_t sA = 0, int64_t sB = 0, int64_t sC = 0)
 {
-    if (M <= 0 || N <= 0)
+    if (M <= 0 || N <= 0 || batch <= 0)
         return;
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER>), grid, dim3(256), 0, st, M, N, K, alpha, A, lda,
-                       B, ldb, beta, C, ldc);
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
+    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER>), grid, dim3(256), 0, st, M, N, K, alpha, A, lda, sA,
+                       B, ldb, sB, beta, C, ldc, sC);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,39 +189,44 @@ __global__ __launch_bounds__(256) void k_fill0(double *a, int64_t total)
 
 // ---------------------------------------------------------------------------
 // Cholesky of the 64 x 64 diagonal block at (k0, k0), in place (lower): the
-// trailing updates of earlier panels are already applied.
+// trailing updates of earlier panels are already applied. One wave, lane i
+// holding row i in registers; column j's entries are broadcast lane by lane
+// (no barriers).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_potrf_diag(double *A, int64_t n, int64_t k0)
+__device__ __forceinline__ double bcast(double v, int src);
+
+__global__ __launch_bounds__(64) void k_potrf_diag(double *A, int64_t n, int64_t k0)
 {
-    __shared__ double a[kNb][kNb + 1];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < kNb * kNb; e += 256)
-        a[e / kNb][e % kNb] = A[(k0 + e / kNb) * n + k0 + e % kNb];
-    __syncthreads();
+    const int i = threadIdx.x;
+    double a[kNb];
+    double *row = A + (k0 + i) * n + k0;
+#pragma unroll
+    for (int l = 0; l < kNb; ++l)
+        a[l] = row[l];
+#pragma unroll
     for (int j = 0; j < kNb; ++j) {
-        if (tid == 0)
-            a[j][j] = sqrt(a[j][j]);
-        __syncthreads();
-        if (tid > j && tid < kNb)
-            a[tid][j] /= a[j][j];
-        __syncthreads();
-        // trailing update of the block: a[i][l] -= a[i][j] a[l][j], j < l <= i
-        for (int e = tid; e < kNb * kNb; e += 256) {
-            const int i = e / kNb, l = e % kNb;
-            if (l > j && i >= l)
-                a[i][l] -= a[i][j] * a[l][j];
+        const double d = sqrt(bcast(a[j], j));
+        if (i == j)
+            a[j] = d;
+        else if (i > j)
+            a[j] /= d;
+#pragma unroll
+        for (int l = j + 1; l < kNb; ++l) {
+            const double c = bcast(a[j], l);        // L[l][j]
+            if (i >= l)
+                a[l] -= a[j] * c;
         }
-        __syncthreads();
     }
-    for (int e = tid; e < kNb * kNb; e += 256) {
-        const int i = e / kNb, l = e % kNb;
+#pragma unroll
+    for (int l = 0; l < kNb; ++l)
         if (l <= i)
-            A[(k0 + i) * n + k0 + l] = a[i][l];
-    }
+            row[l] = a[l];
 }
 
-// Rows below the diagonal block: A[r][k0..k0+63] <- A[r][k0..] L_kk^-T
-// (forward substitution along the row), one row per thread, L_kk in LDS.
+// Rows below the diagonal block: A[r][k0..k0+63] <- A[r][k0..] L_kk^-T, one
+// row per thread with L_kk in LDS. Right-looking along the row: once x_j is
+// final it is removed from every later entry, so the updates of a step are
+// independent of each other.
 __global__ __launch_bounds__(64) void k_trsm_panel(double *A, int64_t n, int64_t k0)
 {
     __shared__ double l[kNb][kNb + 1];
@@ -220,11 +243,10 @@ __global__ __launch_bounds__(64) void k_trsm_panel(double *A, int64_t n, int64_t
         x[j] = row[j];
 #pragma unroll
     for (int j = 0; j < kNb; ++j) {
-        double s = x[j];
+        x[j] /= l[j][j];
 #pragma unroll
-        for (int q = 0; q < j; ++q)
-            s -= x[q] * l[j][q];
-        x[j] = s / l[j][j];
+        for (int q = j + 1; q < kNb; ++q)
+            x[q] -= x[j] * l[q][j];
     }
 #pragma unroll
     for (int j = 0; j < kNb; ++j)
@@ -280,16 +302,25 @@ __device__ __forceinline__ double wave_min(double v)
     return v;
 }
 
-__global__ __launch_bounds__(256) void k_gptq_block(double *__restrict__ Wc, const double *__restrict__ U,
-                                                    int64_t out, int64_t in, int64_t b, int bits, int group,
-                                                    int mode, double *__restrict__ E,
-                                                    uint32_t *__restrict__ qweight, float *__restrict__ scales,
-                                                    uint8_t *__restrict__ zeros)
+constexpr int kRowsPerGroup = 16;   // rows (waves) per workgroup of the column loop
+
+__global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__restrict__ Wc,
+                                                                    const double *__restrict__ U, int64_t out,
+                                                                    int64_t in, int64_t b, int bits, int group,
+                                                                    int mode, double *__restrict__ E,
+                                                                    uint32_t *__restrict__ qweight,
+                                                                    float *__restrict__ scales,
+                                                                    uint8_t *__restrict__ zeros)
 {
+    // U[b : b + 128][b : b + 128] for every row of the workgroup (128 KB)
+    __shared__ double Us[kCol][kCol];
+    for (int e = threadIdx.x; e < kCol * kCol; e += kRowsPerGroup * 64)
+        Us[e / kCol][e % kCol] = U[(b + e / kCol) * in + b + e % kCol];
+    __syncthreads();
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t o = (int64_t)blockIdx.x * 4 + wv;
+    const int64_t o = (int64_t)blockIdx.x * kRowsPerGroup + wv;
     if (o >= out)
-        return;                                    // whole wave; no block-level barrier below
+        return;                                    // whole wave; no barrier below
     double *row = Wc + o * in + b;
     double w0 = row[lane], w1 = row[64 + lane];
     double e0 = 0.0, e1 = 0.0;
@@ -341,15 +372,14 @@ __global__ __launch_bounds__(256) void k_gptq_block(double *__restrict__ Wc, con
             wq = scale * q;
             code = (uint32_t)((int)q + (1 << (bits - 1)));
         }
-        const double err = (w - wq) / U[j * in + j];
+        const double err = (w - wq) / Us[jj][jj];
         if (lane == owner) {
             if (jj < 64) { e0 = err; c0 = code; } else { e1 = err; c1 = code; }
         }
-        const double *urow = U + j * in + b;
         if (lane > jj)
-            w0 -= err * urow[lane];
+            w0 -= err * Us[jj][lane];
         if (64 + lane > jj)
-            w1 -= err * urow[64 + lane];
+            w1 -= err * Us[jj][64 + lane];
     }
     E[o * kCol + lane] = e0;
     E[o * kCol + 64 + lane] = e1;
@@ -399,17 +429,17 @@ static unsigned stream_blocks(int64_t total)
     return (unsigned)(b < 65536 ? (b > 0 ? b : 1) : 65536);
 }
 
-// U = J L^-1 J, L the lower Cholesky factor of J H J. ws: n*n + 64*n doubles.
+// U = J L^-1 J, L the lower Cholesky factor of J H J. ws: n*n + n*n/4 doubles.
 hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws, hipStream_t st)
 {
     const int64_t total = n * n;
     double *Lr = ws;                       // J H J, then (lower part) its Cholesky factor
-    double *T = ws + total;                // 64 x n bracket of the inverse recurrence
+    double *T = ws + total;                // products of the inverse's doubling steps (n*n/4)
     hipLaunchKernelGGL(k_reverse_copy, dim3(stream_blocks(total)), dim3(256), 0, st, H, Lr, total);
     const int64_t nb = n / kNb;
     for (int64_t k = 0; k < nb; ++k) {
         const int64_t k0 = k * kNb, rest = n - k0 - kNb;
-        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, st, Lr, n, k0);
+        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(64), 0, st, Lr, n, k0);
         if (rest > 0) {
             hipLaunchKernelGGL(k_trsm_panel, dim3((unsigned)((rest + 63) / 64)), dim3(64), 0, st, Lr, n, k0);
             // trailing lower triangle -= P P^T, P = the panel below the diagonal block
@@ -418,16 +448,32 @@ hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws,
                                                      Lr + (k0 + kNb) * n + k0 + kNb, n, st);
         }
     }
-    // Li = L^-1 in U's buffer: zero, invert the diagonal blocks, then block row
-    // by block row Li[I][:I] = -Li[I][I] (L[I][:I] Li[:I][:I]).
+    // Li = L^-1 in U's buffer, bottom up: invert the 64 x 64 diagonal blocks,
+    // then, with the inverses of every aligned run of s blocks known, combine
+    // neighbouring runs A (first) and C (second) into the inverse of their
+    // union: its lower-left part is -C^-1 (L21 A^-1). Each level is two batched
+    // GEMMs (T = L21 A^-1 into scratch, then -C^-1 T); a last, shorter run is
+    // combined on its own.
     double *Li = U;
+    double *Tb = T;
     hipLaunchKernelGGL(k_fill0, dim3(stream_blocks(total)), dim3(256), 0, st, Li, total);
     hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, Lr, Li, n);
-    for (int64_t I = 1; I < nb; ++I) {
-        const int64_t r0 = I * kNb;
-        dgemm<double, double, false, false, false>(kNb, r0, r0, 1.0, Lr + r0 * n, n, Li, n, 0.0, T, n, st);
-        dgemm<double, double, false, false, false>(kNb, r0, kNb, -1.0, Li + r0 * n + r0, n, T, n, 0.0,
-                                                   Li + r0 * n, n, st);
+    for (int64_t s = 1; s < nb; s *= 2) {
+        const int64_t S = s * kNb, full = nb / (2 * s), step = 2 * S * n + 2 * S;
+        if (full > 0) {
+            dgemm<double, double, false, false, false>(S, S, S, 1.0, Lr + S * n, n, Li, n, 0.0, Tb, S, st, full,
+                                                       step, step, S * S);
+            dgemm<double, double, false, false, false>(S, S, S, -1.0, Li + S * n + S, n, Tb, S, 0.0, Li + S * n, n,
+                                                       st, full, step, S * S, step);
+        }
+        const int64_t rem = nb - full * 2 * s;
+        if (rem > s) {
+            const int64_t base = full * 2 * S, S2 = (rem - s) * kNb;
+            dgemm<double, double, false, false, false>(S2, S, S, 1.0, Lr + (base + S) * n + base, n,
+                                                       Li + base * n + base, n, 0.0, Tb, S, st);
+            dgemm<double, double, false, false, false>(S2, S, S2, -1.0, Li + (base + S) * n + base + S, n, Tb, S,
+                                                       0.0, Li + (base + S) * n + base, n, st);
+        }
     }
     hipLaunchKernelGGL(k_reverse_inplace, dim3(stream_blocks(total / 2)), dim3(256), 0, st, U, total);
     return hipGetLastError();
@@ -460,8 +506,9 @@ hipError_t launch_gptq_quantize(const void *W, int dtype, int64_t out, int64_t i
         break;
     }
     for (int64_t b = 0; b < in; b += kCol) {
-        hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)((out + 3) / 4)), dim3(256), 0, st, Wc, U, out, in, b,
-                           bits, group, mode, E, qweight, scales, zeros);
+        hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)((out + kRowsPerGroup - 1) / kRowsPerGroup)),
+                           dim3(kRowsPerGroup * 64), 0, st, Wc, U, out, in, b, bits, group, mode, E, qweight,
+                           scales, zeros);
         const int64_t rest = in - b - kCol;
         if (rest > 0)   // later columns -= E U[b : b + 128][b + 128 :]
             dgemm<double, double, false, false, false>(out, rest, kCol, -1.0, E, kCol, U + b * in + b + kCol, in,

@@ -74,7 +74,7 @@ def test_hessian(awq, ref, dt, T, n_in):
     assert np.all(np.abs(H - want) <= bound)
 
 
-@pytest.mark.parametrize("n_in,T", [(128, 300), (256, 100), (512, 1000)])
+@pytest.mark.parametrize("n_in,T", [(128, 300), (256, 100), (512, 1000), (384, 500), (640, 700)])
 def test_factor(awq, ref, n_in, T):
     _, _, _, X32 = make(4, n_in, T, "f32", 2)
     H = G.dampen(G.hessian(X32), 0.01)
