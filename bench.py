@@ -118,7 +118,11 @@ N_CLIP, MAX_SHRINK = 20, 0.5
 def clip_measure(awq, torch, spec, W, X, s_best, args):
     """The clipping-range search on W diag(s_best) (the step after the alpha
     search) and the clipped pack: kernel times from HIP events on the launch
-    stream, and the fp32 MFMA roofline of the search kernel."""
+    stream, and the MFMA roofline of the search kernel. For 16-bit layers the
+    kernel multiplies X by D split into 16-bit parts (two fp16 parts, three
+    bf16 parts) on the 16-bit matrix cores: the roofline takes that dtype's
+    peak with the algorithmic FLOP count, so at most 1/parts of it is
+    reachable; `mfma_issued_frac` counts the parts."""
     out, n_in, T = spec.out, spec.inn, spec.tokens
     dev = W.device
     clip = torch.empty((out, n_in // spec.group), dtype=torch.float32, device=dev)
@@ -155,10 +159,12 @@ def clip_measure(awq, torch, spec, W, X, s_best, args):
     e_best = e.min(dim=-1).values
     macs = N_CLIP * T * out * n_in
     achieved = 2.0 * macs / (ms * 1e-3) / 1e12
+    peak, parts = {"f16": (PEAK_F16_TFLOPS, 2), "bf16": (PEAK_F16_TFLOPS, 3)}.get(spec.dtype, (PEAK_F32_TFLOPS, 1))
     return {"n_clip": N_CLIP, "max_shrink": MAX_SHRINK, "ms": ms, "pack_ms": pack_ms,
             "ratio_macs_per_s": macs / (ms * 1e-3),
             "roofline": {"bound": "mfma", "kernel": "k_clip_search", "achieved": achieved,
-                         "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS,
+                         "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                         "mfma_parts": parts, "mfma_issued_frac": parts * achieved / peak,
                          "traffic": traffic_from_profile(spec.name, CLIP_PMC_FILE, CLIP_SRC)},
             "clipped_group_frac": float((clip < 1).float().mean().item()),
             "group_sse_vs_unclipped": float(e_best.sum() / e[..., 0].sum())}

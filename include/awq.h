@@ -175,12 +175,15 @@ int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const f
  *               Python binding: 20 and 0.5).
  *   clip:       device fp32[out][in / group] (output): the chosen ratios.
  *   sse:        device fp64[out][in / group][n_clip] (output), or NULL.
- * The kernel forms Wq - W from the same fp32 quantizer as awq_quantize_pack,
- * multiplies it with X in fp32 MFMA operations (fp32 accumulation over a
- * group) and sums the squares over tokens in fp64 in a fixed order:
- * bitwise reproducible, each sse within a few group-length multiples of fp32
- * rounding of the exact value; where two ratios' errors lie that close the
- * choice between them may differ from an exact evaluation.
+ * The kernel forms Wq - W in fp32 from the same quantizer as awq_quantize_pack
+ * and multiplies it with X on the matrix cores, accumulating in fp32 over a
+ * group: for fp16 X with Wq - W (scaled by a power of two per row) split into
+ * two fp16 parts (22 significant bits), for bf16 X split exactly into three
+ * bf16 parts, for fp32 X in fp32. The squares are summed over tokens in fp32
+ * per 4 tokens, then in fp64, in a fixed order: bitwise reproducible, each
+ * sse within a few group-length multiples of fp32 rounding of the exact
+ * value; where two ratios' errors lie that close the choice between them may
+ * differ from an exact evaluation.
  * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128}, or more than 65535 groups. */
 int awq_clip_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                     int64_t tokens, const float *s, int bits, int group, int mode, int n_clip,

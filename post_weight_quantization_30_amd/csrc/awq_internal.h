@@ -42,6 +42,18 @@ __device__ __forceinline__ void widen8(const typename Vec8<T>::type &v, float *f
         f[i] = static_cast<float>(v[i]);
 }
 
+// An fp32 value made opaque to instruction selection. Around a multiply the
+// compiler otherwise folds an fp16 widening or narrowing into a mixed-precision
+// fma with a +0 addend: that turns -0 * s into +0 and rounds the exact product
+// once to fp16 instead of first to fp32 -- and it may do so for one use of a
+// narrowed value and not for another, so that the "same" fp16 value differs
+// between them.
+__device__ __forceinline__ float opaque(float x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Workspace layout of awq_search (each part 256-byte aligned).
 struct SearchWs {
     size_t s_off, inv_off, unit_off, part_off, total;

@@ -53,17 +53,6 @@ template <> struct StoreVec8<bf16> {
     }
 };
 
-// An fp32 value made opaque to instruction selection. Around a multiply the
-// compiler may otherwise fold the fp16 widening or the final fp16 narrowing
-// into a mixed-precision fma with a +0 addend: that turns -0 * s into +0 and
-// rounds the product once to fp16 instead of first to fp32 (the operation
-// order stated above).
-__device__ __forceinline__ float opaque(float x)
-{
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 template <typename T, bool COLS>
 __global__ __launch_bounds__(256) void k_fold_vec(const T *A, T *out, int64_t cols, const float *s,
                                                   int64_t nchunk)

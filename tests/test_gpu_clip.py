@@ -7,12 +7,22 @@ Bars:
   * chosen ratio: the oracle's, unless the oracle's errors at the two picks
     differ by less than the two bounds together (a tie within rounding).
 
-Error bound. The kernel forms d = Wq - W in fp32 (3 roundings, relative),
-multiplies X by d in fp32 MFMA steps of 4 products each, accumulating over a
-group of G columns (at most 5 roundings per step, each relative to a partial
-sum bounded by sum_j |x_j d_j|), and sums squares in fp64. Per token
-    |y_gpu - y| <= delta = (2 G + 8) u sum_j |x_tj d_j|,   u = 2^-24,
-(the constant rounds 5 G / 4 + 3 up generously) and so per group
+Error bound. The kernel forms d = Wq - W in fp32 (3 roundings, relative)
+and multiplies X by it on the matrix cores, accumulating in fp32 over a group
+of G columns with at most one rounding per product (each relative to a
+partial sum bounded by sum_j |x_j d_j|); the four squares of a lane's tile
+are summed in fp32 (4 roundings) and the totals in fp64. Per input type:
+  * fp32: d itself, steps of 4 products -> 5 G / 4 + 3 roundings;
+  * bf16: d = hi + mid + lo exactly (three bf16 parts, products exact) ->
+    3 G + 3;
+  * fp16: 2^k d = hi + lo, two fp16 parts, 2^-22 relative (4 u) plus an
+    absolute 2^-25 2^-k where lo is below the fp16 normal range, with 2^k
+    chosen so that 2^k B < 2^14, B = (4 max|v| + max|w s - v|) max(1/s) over
+    the row's group (so 2^-k <= 2^-13 B) -> 2 G + 7 relative roundings.
+With c = 2 G + 8 (fp32), 2 G + 12 (fp16), 3 G + 8 (bf16) -- a few units of
+slack for the fp32 sums of squares -- per token
+    |y_gpu - y| <= delta = c u sum_j |x_tj d_j| + a sum_j |x_tj|,
+a = 2^-38 B for fp16 and 0 otherwise, u = 2^-24, and so per group
     |sse_gpu - sse| <= sum_t (2 |y_t| delta_t + delta_t^2).
 Each test prints the case it runs (flushed) before touching the GPU.
 """
@@ -51,7 +61,7 @@ def f32(arr, dtype):
     return synth.storage_to_f32(arr, dtype)
 
 
-def sse_bounds(ref, Wf, Xf, s, bits, group, mode, n_clip, max_shrink):
+def sse_bounds(ref, Wf, Xf, s, bits, group, mode, n_clip, max_shrink, dt):
     """Per (row, group, ratio): the oracle's exact error and the bound above."""
     out, n_in = Wf.shape
     ng = n_in // group
@@ -59,20 +69,25 @@ def sse_bounds(ref, Wf, Xf, s, bits, group, mode, n_clip, max_shrink):
     ratios = [ref.clip_ratio(i, n_clip, max_shrink) for i in range(n_clip)]
     exact = np.empty((out, ng, n_clip))
     bound = np.empty((out, ng, n_clip))
-    c = 2 * group + 8
+    c = {"f32": 2 * group + 8, "f16": 2 * group + 12, "bf16": 3 * group + 8}[dt]
     for o in range(out):
         for g in range(ng):
             cols = slice(g * group, (g + 1) * group)
             w = Wf[o, cols]
             sg = s[cols]
             v = (w * sg).astype(np.float32)
+            a = 0.0
+            if dt == "f16":
+                perr = np.abs(w.astype(np.float64) * sg - v)
+                inv = (np.float32(1.0) / sg).astype(np.float64)
+                a = 2.0 ** -38 * (4 * np.abs(v).max() + perr.max()) * inv.max() * 1.01
             D = np.empty((n_clip, group))
             for i, r in enumerate(ratios):
                 _, _, _, what = ref.quant_group_clip(v, bits, mode, r)
                 D[i] = what.astype(np.float64) / sg.astype(np.float64) - w.astype(np.float64)
             Xg = X64[:, cols]
             Y = Xg @ D.T
-            delta = c * U * (np.abs(Xg) @ np.abs(D).T)
+            delta = c * U * (np.abs(Xg) @ np.abs(D).T) + a * np.abs(Xg).sum(axis=1)[:, None]
             exact[o, g] = (Y * Y).sum(axis=0)
             bound[o, g] = (2 * np.abs(Y) * delta + delta * delta).sum(axis=0)
     return exact, bound
@@ -111,6 +126,10 @@ CLIP_CASES = [
     ("f16 asym 5-bit g64, 64 ratios", 24, 256, 48, "f16", 5, 64, "asym", 64, 0.9, 16),
     ("bf16 sym g128, 13 ratios", 16, 384, 520, "bf16", 4, 128, "sym", 13, 0.3, 17),
     ("f32 asym g32, one ratio", 5, 64, 20, "f32", 4, 32, "asym", 1, 0.5, 18),
+    # more ratios than the waves hold at once, and more tokens than one chunk
+    ("f16 asym g128, 40 ratios, 600 tokens", 24, 256, 600, "f16", 4, 128, "asym", 40, 0.6, 19),
+    ("f32 sym g128, 30 ratios, 300 tokens", 20, 256, 300, "f32", 4, 128, "sym", 30, 0.5, 20),
+    ("bf16 sym g64, 64 ratios, 7 tokens", 18, 128, 7, "bf16", 4, 64, "sym", 64, 0.95, 21),
 ]
 
 
@@ -129,7 +148,7 @@ def test_clip_search_matches_oracle(awq, ref, case):
     lay, s = make_case(out, n_in, T, dt, bits, group, mode, seed)
     Wf, Xf = f32(lay["W"], dt), f32(lay["X"], dt)
     clip_o, sse_o = ref.clip_search(Wf, Xf, s, bits, group, mode, n_clip, ms)
-    exact, bound = sse_bounds(ref, Wf, Xf, s, bits, group, mode, n_clip, ms)
+    exact, bound = sse_bounds(ref, Wf, Xf, s, bits, group, mode, n_clip, ms, dt)
     say("clip search", name)
     Wd, Xd, sd = dev(lay["W"], dt), dev(lay["X"], dt), torch.from_numpy(s).cuda()
     clip_g, sse_g = awq.clip_search(Wd, Xd, sd, bits, group, mode, n_clip, ms, want_sse=True)
@@ -232,7 +251,7 @@ def test_clip_search_full_size(awq, ref, cfg):
         Wf = f32(lay["W"][a:b], spec.dtype)
         say("clip full size sample rows", spec.name, a, b)
         clip_o, sse_o = ref.clip_search(Wf, Xf, s, spec.bits, spec.group, spec.mode, 20, 0.5)
-        exact, bound = sse_bounds(ref, Wf, Xf, s, spec.bits, spec.group, spec.mode, 20, 0.5)
+        exact, bound = sse_bounds(ref, Wf, Xf, s, spec.bits, spec.group, spec.mode, 20, 0.5, spec.dtype)
         check_clip(clip_g[a:b], sse_g[a:b], clip_o, sse_o, exact, bound, 20, 0.5, ref,
                    f"{spec.name} rows {a}:{b}")
         c2, e2 = awq.clip_search(Wd[a:b].contiguous(), Xd, sb, spec.bits, spec.group, spec.mode, 20,
