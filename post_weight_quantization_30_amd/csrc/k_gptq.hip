@@ -189,68 +189,80 @@ __global__ __launch_bounds__(256) void k_fill0(double *a, int64_t total)
 
 // ---------------------------------------------------------------------------
 // Cholesky of the 64 x 64 diagonal block at (k0, k0), in place (lower): the
-// trailing updates of earlier panels are already applied. One wave, lane i
-// holding row i in registers; column j's entries are broadcast lane by lane
-// (no barriers).
+// trailing updates of earlier panels are already applied. Four waves, one per
+// SIMD: lane i holds row i, wave w its columns l = 4t + w (t < 16). Step j:
+// the wave owning column j forms L[i][j] (the pivot's square root broadcast
+// from lane j) and publishes the column through LDS (double-buffered, so one
+// barrier per step suffices); every wave then removes L[i][j] L[l][j] from
+// its later columns. Entries above the diagonal are carried as scratch and
+// never written back.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double bcast(double v, int src);
 
-__global__ __launch_bounds__(64) void k_potrf_diag(double *A, int64_t n, int64_t k0)
+__global__ __launch_bounds__(256) void k_potrf_diag(double *A, int64_t n, int64_t k0)
 {
-    const int i = threadIdx.x;
-    double a[kNb];
+    __shared__ double colb[2][kNb];
+    const int i = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    double a[kNb / 4];
     double *row = A + (k0 + i) * n + k0;
 #pragma unroll
-    for (int l = 0; l < kNb; ++l)
-        a[l] = row[l];
+    for (int t = 0; t < kNb / 4; ++t)
+        a[t] = 4 * t + w <= i ? row[4 * t + w] : 0.0;
 #pragma unroll
     for (int j = 0; j < kNb; ++j) {
-        const double d = sqrt(bcast(a[j], j));
-        if (i == j)
-            a[j] = d;
-        else if (i > j)
-            a[j] /= d;
-#pragma unroll
-        for (int l = j + 1; l < kNb; ++l) {
-            const double c = bcast(a[j], l);        // L[l][j]
-            if (i >= l)
-                a[l] -= a[j] * c;
+        double *cb = colb[j & 1];
+        if (w == (j & 3)) {
+            // 1/sqrt of the pivot once, then products (no fp64 divide on the
+            // step's serial path)
+            const double p = bcast(a[j >> 2], j);
+            const double rs = rsqrt(p);
+            double v = a[j >> 2];
+            v = i == j ? p * rs : (i > j ? v * rs : v);
+            a[j >> 2] = v;
+            cb[i] = v;                             // L[i][j] for i >= j
         }
+        __syncthreads();
+        const double lij = cb[i];
+#pragma unroll
+        for (int t = 0; t < kNb / 4; ++t)
+            if (4 * t + w > j)                     // uniform per wave
+                a[t] -= lij * cb[4 * t + w];
     }
 #pragma unroll
-    for (int l = 0; l < kNb; ++l)
-        if (l <= i)
-            row[l] = a[l];
+    for (int t = 0; t < kNb / 4; ++t)
+        if (4 * t + w <= i)
+            row[4 * t + w] = a[t];
 }
 
-// Rows below the diagonal block: A[r][k0..k0+63] <- A[r][k0..] L_kk^-T, one
-// row per thread with L_kk in LDS. Right-looking along the row: once x_j is
-// final it is removed from every later entry, so the updates of a step are
-// independent of each other.
-__global__ __launch_bounds__(64) void k_trsm_panel(double *A, int64_t n, int64_t k0)
+// Rows below the diagonal block: A[r][k0..k0+63] <- A[r][k0..] L_kk^-T. One
+// wave per row, lane q holding entry q; step j: x_j = x_j / L[j][j] is
+// broadcast from lane j and removed from the later entries (x_q -= x_j L[q][j]),
+// L_kk and 1/diag in LDS.
+constexpr int kTrsmRows = 8;     // rows (waves) per workgroup
+
+__global__ __launch_bounds__(kTrsmRows * 64) void k_trsm_panel(double *A, int64_t n, int64_t k0)
 {
     __shared__ double l[kNb][kNb + 1];
-    for (int e = threadIdx.x; e < kNb * kNb; e += 64)
+    __shared__ double rd[kNb];
+    for (int e = threadIdx.x; e < kNb * kNb; e += kTrsmRows * 64)
         l[e / kNb][e % kNb] = A[(k0 + e / kNb) * n + k0 + e % kNb];
     __syncthreads();
-    const int64_t r = k0 + kNb + (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (threadIdx.x < kNb)
+        rd[threadIdx.x] = 1.0 / l[threadIdx.x][threadIdx.x];
+    __syncthreads();
+    const int q = threadIdx.x & 63;
+    const int64_t r = k0 + kNb + (int64_t)blockIdx.x * kTrsmRows + (threadIdx.x >> 6);
     if (r >= n)
-        return;
-    double x[kNb];
-    double *row = A + r * n + k0;
-#pragma unroll
-    for (int j = 0; j < kNb; ++j)
-        x[j] = row[j];
+        return;                                    // whole wave, after the barriers
+    double *p = A + r * n + k0 + q;
+    double x = *p;
 #pragma unroll
     for (int j = 0; j < kNb; ++j) {
-        x[j] /= l[j][j];
-#pragma unroll
-        for (int q = j + 1; q < kNb; ++q)
-            x[q] -= x[j] * l[q][j];
+        const double xj = bcast(x, j) * rd[j];
+        x = q == j ? xj : (q > j ? fma(-xj, l[q][j], x) : x);
     }
-#pragma unroll
-    for (int j = 0; j < kNb; ++j)
-        row[j] = x[j];
+    *p = x;
 }
 
 // Inverse of every 64 x 64 diagonal block of the lower triangular L (one block
@@ -314,8 +326,12 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__res
 {
     // U[b : b + 128][b : b + 128] for every row of the workgroup (128 KB)
     __shared__ double Us[kCol][kCol];
+    __shared__ double rdiag[kCol];       // 1 / U[j][j]: the error's scaling without a division per column
     for (int e = threadIdx.x; e < kCol * kCol; e += kRowsPerGroup * 64)
         Us[e / kCol][e % kCol] = U[(b + e / kCol) * in + b + e % kCol];
+    __syncthreads();
+    if (threadIdx.x < kCol)
+        rdiag[threadIdx.x] = 1.0 / Us[threadIdx.x][threadIdx.x];
     __syncthreads();
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t o = (int64_t)blockIdx.x * kRowsPerGroup + wv;
@@ -372,7 +388,7 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__res
             wq = scale * q;
             code = (uint32_t)((int)q + (1 << (bits - 1)));
         }
-        const double err = (w - wq) / Us[jj][jj];
+        const double err = (w - wq) * rdiag[jj];
         if (lane == owner) {
             if (jj < 64) { e0 = err; c0 = code; } else { e1 = err; c1 = code; }
         }
@@ -439,9 +455,10 @@ hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws,
     const int64_t nb = n / kNb;
     for (int64_t k = 0; k < nb; ++k) {
         const int64_t k0 = k * kNb, rest = n - k0 - kNb;
-        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(64), 0, st, Lr, n, k0);
+        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, st, Lr, n, k0);
         if (rest > 0) {
-            hipLaunchKernelGGL(k_trsm_panel, dim3((unsigned)((rest + 63) / 64)), dim3(64), 0, st, Lr, n, k0);
+            hipLaunchKernelGGL(k_trsm_panel, dim3((unsigned)((rest + kTrsmRows - 1) / kTrsmRows)),
+                               dim3(kTrsmRows * 64), 0, st, Lr, n, k0);
             // trailing lower triangle -= P P^T, P = the panel below the diagonal block
             const double *P = Lr + (k0 + kNb) * n + k0;
             dgemm<double, double, false, true, true>(rest, rest, kNb, -1.0, P, n, P, n, 1.0,
