@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__res
     const double maxq = (double)((1 << bits) - 1);
     const double L = (double)((1 << (bits - 1)) - 1);
     const int64_t ng = in / group;
-    double scale = 1.0, zero = 0.0;
+    double scale = 1.0, zero = 0.0, rscale = 1.0;
     for (int jj = 0; jj < kCol; ++jj) {
         const int64_t j = b + jj;
         if (jj % group == 0) {
@@ -361,6 +361,7 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__res
                 s64 = fmax((hi - lo) / maxq, 1e-8);
                 scale = (double)(float)s64;
                 zero = rint(-lo / scale);
+                rscale = 1.0 / scale;
             } else {
                 double a = 0.0;
                 if (in0) a = fmax(a, fabs(w0));
@@ -369,6 +370,7 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__res
                 s64 = fmax(a / L, 1e-8);
                 scale = (double)(float)s64;
                 zero = (double)(1 << (bits - 1));
+                rscale = 1.0 / scale;
             }
             if (lane == 0) {
                 scales[o * ng + j / group] = (float)scale;
@@ -377,14 +379,22 @@ __global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__res
         }
         const int owner = jj & 63;
         const double w = bcast(jj < 64 ? w0 : w1, owner);
+        // rint(w / scale) off the division's latency: t = w * (1/scale) is
+        // within 3 ulp of the quotient, so the two round to the same integer
+        // unless t lies within 1e-9 of a half-integer (true for |t| < 2^20;
+        // larger quotients are clamped to the code range either way); there,
+        // and at exact ties, the quotient itself decides
+        double r = rint(w * rscale);
+        if (fabs(fabs(w * rscale - r) - 0.5) < 1e-9)
+            r = rint(w / scale);
         double q, wq;
         uint32_t code;
         if (mode == AWQ_ASYM) {
-            q = fmin(fmax(rint(w / scale) + zero, 0.0), maxq);
+            q = fmin(fmax(r + zero, 0.0), maxq);
             wq = scale * (q - zero);
             code = (uint32_t)(int)q;
         } else {
-            q = fmin(fmax(rint(w / scale), -L - 1.0), L);
+            q = fmin(fmax(r, -L - 1.0), L);
             wq = scale * q;
             code = (uint32_t)((int)q + (1 << (bits - 1)));
         }
