@@ -209,15 +209,15 @@ def fold_measure(awq, torch, spec, W, s_best, args):
 
 def qgemm_measure(awq, torch, spec, X, qweight, scales, zeros, s_best, args):
     """The deployment product over the layer's packed result: decode (1 and 16
-    tokens, HBM-bound: the packed weights are read once) and 256 tokens (MFMA).
-    Launches are captured in a HIP graph so that the host's per-call overhead
-    does not hide the kernel time; the graph's result is checked against an
-    eager call."""
+    tokens, HBM-bound: the packed weights are read once), 256 tokens and a
+    2048-token prefill (MFMA; the calibration tokens repeated). Launches are
+    captured in a HIP graph so that the host's per-call overhead does not hide
+    the kernel time; the graph's result is checked against an eager call."""
     out, n_in = spec.out, spec.inn
     Xin = (X.float() / s_best[None, :]).to(X.dtype).contiguous()      # 1/s folded upstream
     res = {}
-    for M in (1, 16, 256):
-        xm = Xin[:M].contiguous()
+    for M in (1, 16, 256, 2048):
+        xm = Xin.repeat((M + Xin.shape[0] - 1) // Xin.shape[0], 1)[:M].contiguous()
         y = torch.empty((M, out), dtype=X.dtype, device=X.device)
         awq.qgemm(xm, qweight, scales, zeros, spec.bits, spec.group, y=y)
         torch.cuda.synchronize()

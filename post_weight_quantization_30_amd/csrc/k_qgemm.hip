@@ -364,6 +364,207 @@ __global__ __launch_bounds__(kQWaves * 64) void k_qgemm(const TX *__restrict__ X
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill (many tokens): one block = 64 tokens x 128 output rows over all of
+// K, wave w taking rows 16 w .. +15 for all four 16-token tiles. K runs in
+// chunks of 128 columns: X (64 x 128) and the packed codes of the 128 rows
+// (plus their scales and zeros) are loaded into registers one chunk ahead and
+// staged through LDS (double-buffered, one barrier per chunk; fp16 X is
+// stored already in the operand order of the code pairs); each wave builds
+// the (code - zero) operands of its row tile from the staged codes exactly as
+// the decode kernel does and multiplies them with the X fragments of the four
+// token tiles, one group at a time, each group's fp32 sums scaled once into
+// the totals. Every staged X value serves 128 rows and every built operand 64
+// tokens.
+// ---------------------------------------------------------------------------
+constexpr int kPfM = 64, kPfN = 128, kPfK = 128;
+
+template <int BITS>
+struct PfStage {
+    static constexpr int XROW = kPfK * 2 + 16;                  // LDS bytes per token row (padded)
+    static constexpr int XB = kPfM * XROW;
+    static constexpr int CRB = kPfK * BITS / 8;                 // code bytes of one row in a chunk
+    static constexpr int CROW = CRB + 16;
+    static constexpr int CB = kPfN * CROW;
+    static constexpr int NGMAX = kPfK / 32;                     // groups per chunk at most
+    static constexpr int BUF = XB + CB + kPfN * NGMAX * 4 + kPfN * NGMAX;
+    static constexpr int XCH = kPfM * kPfK * 2 / 16 / (kQWaves * 64);   // 16-byte X chunks per thread (2)
+    static constexpr int CCH = kPfN * CRB / 16 / (kQWaves * 64);        // 16-byte code chunks per thread
+};
+
+template <typename TX, int BITS, int G, bool YF32>
+__global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf(const TX *__restrict__ X, int64_t M, int64_t in,
+                                                           const uint32_t *__restrict__ qweight,
+                                                           const float *__restrict__ scales,
+                                                           const uint8_t *__restrict__ zeros, int64_t out,
+                                                           void *__restrict__ Y)
+{
+    typedef PfStage<BITS> S;
+    typedef typename QOp<TX>::vec vec;
+    constexpr int GPC = kPfK / G;               // groups per chunk
+    constexpr int STEPS = G / 32;
+    constexpr int GB = G * BITS / 8;            // code bytes of one group of one row
+    constexpr int WPL = G * BITS / 128;         // code words per lane per group
+    constexpr uint32_t cmask = (1u << BITS) - 1u;
+    constexpr bool kPairs = std::is_same<TX, f16>::value;
+    __shared__ __align__(16) uint8_t lds[2 * S::BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, c = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.y * kPfM, n0 = (int64_t)blockIdx.x * kPfN;
+    const int64_t ng = in / G, row_bytes = in * BITS / 8;
+    const int64_t chunks = in / kPfK;
+    const uint8_t *qbytes = reinterpret_cast<const uint8_t *>(qweight);
+
+    // registers of the chunk in flight (rows and tokens past the end load the
+    // last row/token; their results are never stored)
+    u32x4 xr[S::XCH], cr[S::CCH];
+    float sr = 0.f;
+    uint8_t zr = 0;
+    auto fetch = [&](int64_t kc) {
+#pragma unroll
+        for (int i = 0; i < S::XCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            int64_t m = m0 + ch / (kPfK * 2 / 16);
+            m = m < M ? m : M - 1;
+            xr[i] = *reinterpret_cast<const u32x4 *>(X + m * in + kc * kPfK + (ch % (kPfK * 2 / 16)) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < S::CCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            int64_t n = n0 + ch / (S::CRB / 16);
+            n = n < out ? n : out - 1;
+            cr[i] = *reinterpret_cast<const u32x4 *>(qbytes + n * row_bytes + kc * S::CRB + (ch % (S::CRB / 16)) * 16);
+        }
+        if (tid < kPfN * GPC) {
+            int64_t n = n0 + tid / GPC;
+            n = n < out ? n : out - 1;
+            sr = scales[n * ng + kc * GPC + tid % GPC];
+            zr = zeros[n * ng + kc * GPC + tid % GPC];
+        }
+    };
+    auto stash = [&](uint8_t *buf) {
+#pragma unroll
+        for (int i = 0; i < S::XCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            u32x4 v = xr[i];
+            if constexpr (kPairs) {
+                // a 16-byte chunk is one operand's 8 columns: store them in
+                // the order the code pairs come out in
+                constexpr const int *P = F16Pairs<BITS>::PERM;
+                const vec a = __builtin_bit_cast(vec, v);
+                v = __builtin_bit_cast(u32x4, __builtin_shufflevector(a, a, P[0], P[1], P[2], P[3], P[4], P[5],
+                                                                      P[6], P[7]));
+            }
+            *reinterpret_cast<u32x4 *>(buf + (ch / (kPfK * 2 / 16)) * S::XROW + (ch % (kPfK * 2 / 16)) * 16) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < S::CCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            *reinterpret_cast<u32x4 *>(buf + S::XB + (ch / (S::CRB / 16)) * S::CROW + (ch % (S::CRB / 16)) * 16) = cr[i];
+        }
+        if (tid < kPfN * GPC) {
+            reinterpret_cast<float *>(buf + S::XB + S::CB)[tid] = sr;
+            (buf + S::XB + S::CB + kPfN * S::NGMAX * 4)[tid] = zr;
+        }
+    };
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fetch(0);
+    stash(lds);
+    __syncthreads();
+    for (int64_t kc = 0; kc < chunks; ++kc) {
+        const uint8_t *buf = lds + (kc & 1) * S::BUF;
+        if (kc + 1 < chunks)
+            fetch(kc + 1);
+        const float *sbuf = reinterpret_cast<const float *>(buf + S::XB + S::CB);
+        const uint8_t *zbuf = buf + S::XB + S::CB + kPfN * S::NGMAX * 4;
+        const int row = wave * 16 + r;
+#pragma unroll
+        for (int gq = 0; gq < GPC; ++gq) {
+            // B operands of this wave's row tile for group gq of the chunk
+            uint32_t wv[WPL];
+            const uint8_t *src = buf + S::XB + row * S::CROW + gq * GB + c * (GB / 4);
+            if constexpr (WPL % 4 == 0) {
+#pragma unroll
+                for (int q = 0; q < WPL / 4; ++q) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 16 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wv[4 * q + e] = v[e];
+                }
+            } else if constexpr (WPL == 2) {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
+                wv[0] = v[0];
+                wv[1] = v[1];
+            } else {
+                wv[0] = *reinterpret_cast<const uint32_t *>(src);
+            }
+            const float scale = sbuf[row * GPC + gq];
+            const int zero = zbuf[row * GPC + gq];
+            vec b[STEPS];
+            if constexpr (kPairs) {
+                const f16 zb = static_cast<f16>(1024 + zero);           // exact: at most 1279
+                const f16x2 z2 = {zb, zb};
+                const uint32_t mask = F16Pairs<BITS>::kMask, magic = 0x64006400u;
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st) {
+                    uint32_t u[4];
+                    F16Pairs<BITS>::make(&wv[st * BITS / 4], u, mask, magic);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const f16x2 d = __builtin_bit_cast(f16x2, u[p]) - z2;   // exact
+                        b[st][2 * p] = d[0];
+                        b[st][2 * p + 1] = d[1];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 8 * st + e;
+                        const int code = (int)((wv[(j * BITS) / 32] >> ((j * BITS) % 32)) & cmask);
+                        b[st][e] = static_cast<TX>(static_cast<float>(code - zero));   // exact
+                    }
+            }
+            // the four token tiles: X fragments from LDS (the same k-slot order)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int tok = mt * 16 + r;
+                const uint8_t *xp = buf + tok * S::XROW + (gq * G + c * (G / 4)) * 2;
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st)
+                    part = QOp<TX>::mfma(*reinterpret_cast<const vec *>(xp + 16 * st), b[st], part);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[mt][i] = fmaf(scale, part[i], acc[mt][i]);
+            }
+        }
+        if (kc + 1 < chunks)
+            stash(lds + ((kc + 1) & 1) * S::BUF);
+        __syncthreads();
+    }
+    const int64_t nn = n0 + wave * 16 + r;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = m0 + mt * 16 + 4 * c + i;
+            if (m < M && nn < out) {
+                if (YF32)
+                    static_cast<float *>(Y)[m * out + nn] = acc[mt][i];
+                else
+                    static_cast<TX *>(Y)[m * out + nn] = static_cast<TX>(acc[mt][i]);
+            }
+        }
+}
+
 template <typename TX, int BITS, int G>
 static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t *qweight,
                            const float *scales, const uint8_t *zeros, int64_t out, void *Y, bool yf32,
@@ -372,8 +573,10 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
     const dim3 block(kQWaves * 64);
     // decode (M <= 16): 16 tokens and 16 rows per block, or 32 rows on layers
     // with at least 8192 rows (twice the bytes staged per round; enough blocks
-    // remain to fill the chip); otherwise 64 rows x 32 tokens per block (each
-    // staged row and X fragment reused 4 and 2 times).
+    // remain to fill the chip); the 64-token x 128-row prefill tile when it
+    // gives at least one block per compute unit (and in is a multiple of 128);
+    // otherwise 64 rows x 32 tokens per block (each staged row and X fragment
+    // reused 4 and 2 times, split over K inside the block).
 #define AWQ_QGEMM(MT, NT, YF)                                                                        \
     hipLaunchKernelGGL((k_qgemm<TX, BITS, G, MT, NT, YF>),                                            \
                        dim3((unsigned)((out + 16 * NT - 1) / (16 * NT)),                             \
@@ -383,8 +586,16 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
         if (yf32) AWQ_QGEMM(1, 1, true); else AWQ_QGEMM(1, 1, false);
     } else if (M <= 16) {
         if (yf32) AWQ_QGEMM(1, 2, true); else AWQ_QGEMM(1, 2, false);
-    } else {
+    } else if (M <= 32 || in % kPfK != 0 || ((out + kPfN - 1) / kPfN) * ((M + kPfM - 1) / kPfM) < 256) {
         if (yf32) AWQ_QGEMM(2, 4, true); else AWQ_QGEMM(2, 4, false);
+    } else {
+        const dim3 grid((unsigned)((out + kPfN - 1) / kPfN), (unsigned)((M + kPfM - 1) / kPfM));
+        if (yf32)
+            hipLaunchKernelGGL((k_qgemm_pf<TX, BITS, G, true>), grid, block, 0, st, (const TX *)X, M, in, qweight,
+                               scales, zeros, out, Y);
+        else
+            hipLaunchKernelGGL((k_qgemm_pf<TX, BITS, G, false>), grid, block, 0, st, (const TX *)X, M, in, qweight,
+                               scales, zeros, out, Y);
     }
 #undef AWQ_QGEMM
     return hipGetLastError();

@@ -101,6 +101,13 @@ CASES = [
     ("bf16", 8, 64, "asym", 1, 1, 64),          # a single output row and token
     ("f16", 4, 128, "asym", 3, 8200, 256),      # tall layer: 32-row decode blocks, ragged rows
     ("bf16", 8, 64, "sym", 16, 8192, 128),
+    # the 64-token x 128-row prefill tile (at least 256 blocks, in a multiple of 128)
+    ("bf16", 4, 128, "sym", 1000, 4000, 256),    # ragged token and row tiles
+    ("f16", 8, 64, "asym", 1100, 3900, 128),
+    ("f16", 4, 32, "sym", 2048, 2048, 128),
+    # more than 32 tokens, fewer blocks or in not a multiple of 128: the 32-token tile
+    ("bf16", 4, 128, "sym", 200, 130, 1024),
+    ("f16", 4, 32, "asym", 40, 50, 96),
 ]
 
 
@@ -121,17 +128,19 @@ def test_qgemm_matches_oracle(awq, ref, case, y_f32):
     assert torch.equal(Y, Y2)                       # bitwise reproducible
 
 
-@pytest.mark.parametrize("M", [1, 16, 256])
+@pytest.mark.parametrize("M", [1, 16, 256, 2048])
 def test_qgemm_full_size_layer(awq, ref, M):
     """The 4096x4096 fp16 int4 g128 layer packed from its own search; sampled
-    output rows against the oracle (all rows when M is small)."""
+    output rows against the oracle (all rows when M is small). 2048 tokens
+    (the calibration tokens repeated) take the prefill tile."""
     spec = synth.HEADLINE
     lay = synth.make_layer(spec)
     say("qgemm full size", M)
     Wd = awq.to_device(lay["W"], spec.dtype)
     Xd = awq.to_device(lay["X"], spec.dtype)
     res = awq.quantize_layer(Wd, Xd, spec.bits, spec.group, spec.grid, spec.mode)
-    Xin = awq.fold_rows(Xd.t().contiguous(), res["s_best"]).t().contiguous()[:M]   # X / s
+    Xin = awq.fold_rows(Xd.t().contiguous(), res["s_best"]).t().contiguous()       # X / s
+    Xin = Xin.repeat((M + Xin.shape[0] - 1) // Xin.shape[0], 1)[:M].contiguous()
     Y = awq.qgemm(Xin, res["qweight"], res["scales"], res["zeros"], spec.bits, spec.group, y_f32=True)
     torch.cuda.synchronize()
     q = res["qweight"].cpu().numpy().view(np.uint32)
