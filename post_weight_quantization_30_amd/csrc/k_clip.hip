@@ -13,19 +13,22 @@
 //     sse[o][g][i] = sum_t ( sum_{j in g} X[t, j] * (Q(v)_j / s_j - w_j) )^2
 // is formed; clip[o][g] = r of the first strict minimum.
 //
-// How: one block per (16 rows, one group), 8 waves. Each wave owns whole
-// ratios (ratio j by wave j % 8): it builds their D tiles d = Q(v)/s - w in
-// fp32 (the exact quantizer's operation order, correctly rounded quotients)
-// and keeps them in registers as MFMA B operands; X passes through LDS in
-// chunks of tokens, and every wave multiplies each 16-token tile of it by its
-// tiles and squares the results. The waves on one SIMD (w and w + 4) then
-// share the ratios evenly when n_clip = 20.
+// How: one block per (16 rows, one group), 8 waves, two blocks per compute
+// unit (at most 128 VGPRs per lane, so that one block's loads and barriers
+// hide behind the other's work). Each wave owns whole ratios (ratio j by wave
+// j % 8, in rounds of RW ratios per wave: one at G = 128, more for smaller
+// groups): it builds their D tiles d = Q(v)/s - w in fp32 (the exact
+// quantizer's operation order, correctly rounded quotients) and keeps them in
+// registers as MFMA B operands; X passes through LDS in chunks of 256 tokens
+// (128 for fp32), which stay resident across rounds when one chunk holds all
+// tokens, and every wave multiplies each 16-token tile of it by its tiles and
+// squares the results.
 //
 // Operand precision. Each choice rests on one (row, group) error with no
 // averaging over rows, and adjacent ratios' errors often differ by only 1e-4
 // relative, so D is carried at (near) fp32 precision:
 //   * fp16 X: D (scaled by a power of two 2^k per row, chosen from a bound on
-//     |d| so that k d stays below 2^14) is split into hi = fp16(d') and
+//     |d| so that 2^k |d| stays below 2^14) is split into hi = fp16(d') and
 //     lo = fp16(d' - hi): 22 significant bits, relative error <= 2^-22 (plus
 //     an absolute 2^-25 in d' units where lo falls below the fp16 normal
 //     range); two fp16 MFMAs against the exact fp16 X;
@@ -170,7 +173,7 @@ template <> struct ClipMma<float> {
 template <typename TIn, int G>
 struct ClipShape {
     static constexpr int KS = G / 32;
-    static constexpr int RW = KS == 1 ? (ClipMma<TIn>::NP == 3 ? 8 : 12) : KS == 2 ? (ClipMma<TIn>::NP == 3 ? 4 : 6) : 2;
+    static constexpr int RW = ClipMma<TIn>::NP == 3 ? (KS == 1 ? 2 : 1) : (4 / KS > 0 ? 4 / KS : 1);
     static constexpr int E = (int)sizeof(TIn);
     static constexpr int TOKC = E == 4 ? 128 : 256;            // tokens per LDS chunk
     static constexpr int ROWB = G * E + 16;                     // LDS bytes per token (16-byte pad)
@@ -222,7 +225,7 @@ __device__ __forceinline__ void clip_tile(const typename M::xvec (&a)[KS],
 }
 
 template <typename TIn, int G, bool ASYM>
-__global__ __launch_bounds__(kClipThreads, 1) void k_clip_search(
+__global__ __launch_bounds__(kClipThreads, 2) void k_clip_search(
     const TIn *__restrict__ W, const TIn *__restrict__ X, int64_t out, int64_t in, int64_t tokens,
     const float *__restrict__ s, int bits, int n_clip, float max_shrink, float *__restrict__ clip,
     double *__restrict__ sse_out)
@@ -272,11 +275,7 @@ __global__ __launch_bounds__(kClipThreads, 1) void k_clip_search(
         }                                                                                          \
     } while (0)
 
-    typename Vec8<TIn>::type wr[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        wr[ks] = load8(W + row_c * in + g0 + c * 8 + ks * 32);
-    CLIP_X_FETCH(0);
+    const TIn *wrow = W + row_c * in + g0 + c * 8;
     if (tid < G) {
         const float sv = s[g0 + tid];
         s_l[tid] = sv;
@@ -293,7 +292,7 @@ __global__ __launch_bounds__(kClipThreads, 1) void k_clip_search(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         float w[8];
-        widen8<TIn>(wr[ks], w);
+        widen8<TIn>(load8(wrow + ks * 32), w);
         const f32x8 s8 = *reinterpret_cast<const f32x8 *>(s_l + c * 8 + ks * 32);
         const f32x8 i8 = *reinterpret_cast<const f32x8 *>(inv_l + c * 8 + ks * 32);
 #pragma unroll
@@ -363,7 +362,7 @@ __global__ __launch_bounds__(kClipThreads, 1) void k_clip_search(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             float w[8], v[8], perr[8], inv[8];
-            widen8<TIn>(wr[ks], w);
+            widen8<TIn>(load8(wrow + ks * 32), w);
             const f32x8 s8 = *reinterpret_cast<const f32x8 *>(s_l + c * 8 + ks * 32);
             const f32x8 i8 = *reinterpret_cast<const f32x8 *>(inv_l + c * 8 + ks * 32);
 #pragma unroll
@@ -403,14 +402,11 @@ __global__ __launch_bounds__(kClipThreads, 1) void k_clip_search(
         for (int ch = 0; ch < nch; ++ch) {
             const int64_t t0 = (int64_t)ch * S::TOKC;
             if (!(nch == 1 && r0 > 0)) {          // a single chunk stays resident
+                CLIP_X_FETCH(t0);
                 if (r0 > 0 || ch > 0)
                     __syncthreads();              // the previous chunk is no longer read
                 CLIP_X_STASH(t0);
                 __syncthreads();
-                if (ch + 1 < nch)
-                    CLIP_X_FETCH(t0 + S::TOKC);
-                else if (nch > 1 && r0 + kClipWaves * RW < n_clip)
-                    CLIP_X_FETCH(0);
             }
             const int ntile = (int)((tokens - t0 + 15) / 16 < S::TOKC / 16 ? (tokens - t0 + 15) / 16 : S::TOKC / 16);
             for (int tt = 0; tt < ntile; ++tt) {
