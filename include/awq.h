@@ -97,7 +97,8 @@ int awq_s_table(const float *xmag, int64_t in, int grid, float *s_table, void *s
  * 16-bit (the input type) for fp16/bf16 layers with at least 256 rows and 16
  * tokens, and exact fp32 otherwise (fp32 inputs, or layers too small for the
  * unbiased 16-bit rounding of Wq - W to average out below 1e-3).
- * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128}. */
+ * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128}; W, X or ws not 16-byte
+ * aligned (any allocation is; an offset view need not be). */
 int awq_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                int64_t tokens, const float *xmag, int bits, int group, int grid, int mode,
                double *mse, int32_t *best, float *s_best, void *ws, size_t ws_bytes,
@@ -144,7 +145,8 @@ int awq_search_finish(int64_t out, int64_t in, int64_t tokens, int grid, double 
  *            of 32-bit words; every row starts on a word boundary.
  *   scales:  device fp32[out][in / group] (output).
  *   zeros:   device uint8[out][in / group] (output).
- * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128, 256, 512, 1024, 2048}. */
+ * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128, 256, 512, 1024, 2048}; W or s
+ * not 16-byte aligned. */
 int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s,
                       int bits, int group, int mode, uint32_t *qweight, float *scales,
                       uint8_t *zeros, void *stream);
@@ -184,7 +186,8 @@ int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const f
  * sse within a few group-length multiples of fp32 rounding of the exact
  * value; where two ratios' errors lie that close the choice between them may
  * differ from an exact evaluation.
- * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128}, or more than 65535 groups. */
+ * AWQ_ERR_UNSUPPORTED: group not in {32, 64, 128}, more than 65535 groups, or
+ * W or X not 16-byte aligned. */
 int awq_clip_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                     int64_t tokens, const float *s, int bits, int group, int mode, int n_clip,
                     float max_shrink, float *clip, double *sse, void *stream);

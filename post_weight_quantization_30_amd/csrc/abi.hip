@@ -74,6 +74,11 @@ size_t awq_search_workspace_size(int64_t out, int64_t in, int64_t tokens, int gr
 
 namespace {
 
+// The search, clipping and packing kernels read W, X, s and the workspace in
+// 16-byte vectors: their base addresses must be 16-byte aligned (any
+// allocation is; an offset view need not be).
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 int check_search_shape(int64_t out, int64_t in, int64_t tokens, int grid)
 {
     if (out < 1 || in < 1 || tokens < 1 || grid < 1 || grid > AWQ_MAX_GRID)
@@ -87,6 +92,8 @@ int check_workspace(int64_t out, int64_t in, int64_t tokens, int grid, const voi
     *lay = awq::search_ws_layout(out, in, tokens, grid);
     if (!ws || ws_bytes < lay->total)
         return AWQ_ERR_WORKSPACE;
+    if (!aligned16(ws))
+        return AWQ_ERR_UNSUPPORTED;
     if (lay->nblk > (int64_t)0x7fffffff || (tokens + awq::kTokPerBlock - 1) / awq::kTokPerBlock > 65535 ||
         (in + 255) / 256 > (int64_t)0x7fffffff)
         return AWQ_ERR_UNSUPPORTED;
@@ -99,6 +106,8 @@ int check_candidates(const void *W, const void *X, int dtype, int64_t in, int bi
     if (!W || !X || group < 1 || in % group != 0 || bits < 2 || bits > 8 || !valid_dtype(dtype) ||
         !valid_mode(mode))
         return AWQ_ERR_INVALID_ARG;
+    if (!aligned16(W) || !aligned16(X))
+        return AWQ_ERR_UNSUPPORTED;
     return AWQ_OK;
 }
 
@@ -367,7 +376,7 @@ int awq_quantize_pack_clip(const void *W, int dtype, int64_t out, int64_t in, co
     if (out < 1 || in < 1 || group < 1 || in % group != 0 || bits < 2 || bits > 8 ||
         !valid_dtype(dtype) || !valid_mode(mode))
         return AWQ_ERR_INVALID_ARG;
-    if (!pack_group_ok(group))
+    if (!pack_group_ok(group) || !aligned16(W) || !aligned16(s))
         return AWQ_ERR_UNSUPPORTED;
     if ((out * (in / 32) + 255) / 256 > (int64_t)0x7fffffff)
         return AWQ_ERR_UNSUPPORTED;

@@ -211,3 +211,28 @@ def test_binding_refuses_cpu_tensors(L):
         awq.act_stats(torch.zeros(4, 32))
     with pytest.raises(TypeError):
         awq.quantize_pack(torch.zeros(4, 32), torch.ones(32), 4, 32, "sym")
+
+
+def test_vector_kernels_reject_misaligned_pointers(L):
+    """The search, clipping and packing kernels read W, X, s and the search
+    workspace in 16-byte vectors: a misaligned base is refused on the host
+    (AWQ_ERR_UNSUPPORTED) before anything is enqueued."""
+    from post_weight_quantization_30_amd import awq
+    odd = ctypes.c_void_p(0x10002)
+    f = ctypes.c_float
+    ws = awq.search_workspace_size(64, 256, 32, 20)
+    # search: W, X, ws
+    for W, X, w in ((odd, FAKE, FAKE), (FAKE, odd, FAKE), (FAKE, FAKE, odd)):
+        assert L.awq_search(W, X, 1, 64, 256, 32, FAKE, 4, 128, 20, 0, FAKE, FAKE, FAKE, w, ws, None) == -5
+    assert L.awq_search_candidates(odd, FAKE, 1, 64, 256, 32, 4, 128, 20, 0, FAKE, ws, None) == -5
+    assert L.awq_search_prepare(FAKE, 64, 256, 32, 20, odd, ws, None) == -5
+    assert L.awq_search_finish(64, 256, 32, 20, FAKE, FAKE, FAKE, odd, ws, None) == -5
+    # clipping search: W, X
+    assert L.awq_clip_search(odd, FAKE, 1, 64, 256, 32, FAKE, 4, 128, 0, 20, f(0.5), FAKE, None, None) == -5
+    assert L.awq_clip_search(FAKE, odd, 1, 64, 256, 32, FAKE, 4, 128, 0, 20, f(0.5), FAKE, None, None) == -5
+    # pack: W, s
+    assert L.awq_quantize_pack(odd, 1, 8, 256, FAKE, 4, 128, 0, FAKE, FAKE, FAKE, None) == -5
+    assert L.awq_quantize_pack(FAKE, 1, 8, 256, odd, 4, 128, 0, FAKE, FAKE, FAKE, None) == -5
+    assert L.awq_quantize_pack_clip(odd, 1, 8, 256, FAKE, FAKE, 4, 128, 0, FAKE, FAKE, FAKE, None) == -5
+    # a null pointer is still an invalid argument, not an alignment matter
+    assert L.awq_quantize_pack(None, 1, 8, 256, FAKE, 4, 128, 0, FAKE, FAKE, FAKE, None) == -1
