@@ -575,8 +575,9 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
     // with at least 8192 rows (twice the bytes staged per round; enough blocks
     // remain to fill the chip); the 64-token x 128-row prefill tile when it
     // gives at least one block per compute unit (and in is a multiple of 128);
-    // otherwise 64 rows x 32 tokens per block (each staged row and X fragment
-    // reused 4 and 2 times, split over K inside the block).
+    // otherwise split over K inside the block, 16 tokens x 32 rows up to 32
+    // tokens, 16 x 64 up to 64 and 32 x 64 beyond (measured: the smaller tiles
+    // win while their extra blocks still fit the chip at once).
 #define AWQ_QGEMM(MT, NT, YF)                                                                        \
     hipLaunchKernelGGL((k_qgemm<TX, BITS, G, MT, NT, YF>),                                            \
                        dim3((unsigned)((out + 16 * NT - 1) / (16 * NT)),                             \
@@ -586,7 +587,11 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
         if (yf32) AWQ_QGEMM(1, 1, true); else AWQ_QGEMM(1, 1, false);
     } else if (M <= 16) {
         if (yf32) AWQ_QGEMM(1, 2, true); else AWQ_QGEMM(1, 2, false);
-    } else if (M <= 32 || in % kPfK != 0 || ((out + kPfN - 1) / kPfN) * ((M + kPfM - 1) / kPfM) < 256) {
+    } else if (M <= 32) {
+        if (yf32) AWQ_QGEMM(1, 2, true); else AWQ_QGEMM(1, 2, false);
+    } else if (M <= 64) {
+        if (yf32) AWQ_QGEMM(1, 4, true); else AWQ_QGEMM(1, 4, false);
+    } else if (in % kPfK != 0 || ((out + kPfN - 1) / kPfN) * ((M + kPfM - 1) / kPfM) < 256) {
         if (yf32) AWQ_QGEMM(2, 4, true); else AWQ_QGEMM(2, 4, false);
     } else {
         const dim3 grid((unsigned)((out + kPfN - 1) / kPfN), (unsigned)((M + kPfM - 1) / kPfM));
