@@ -37,6 +37,66 @@ constexpr int kNb = 64;          // Cholesky / inverse panel
 constexpr int kCol = 128;        // GPTQ column block
 
 // ---------------------------------------------------------------------------
+// Cholesky of the 64 x 64 diagonal block at (k0, k0), in place (lower): the
+// trailing updates of earlier panels are already applied. Four waves, one per
+// SIMD: lane i holds row i, wave w its columns l = 4t + w (t < 16). Step j:
+// the wave owning column j forms L[i][j] (the pivot's square root broadcast
+// from lane j) and publishes the column through LDS (double-buffered, so one
+// barrier per step suffices); every wave then removes L[i][j] L[l][j] from
+// its later columns. Entries above the diagonal are carried as scratch and
+// never written back.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double bcast(double v, int src)
+{
+    const long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffffLL), src);
+    const int hi = __builtin_amdgcn_readlane((int)(u >> 32), src);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Needs a 256-thread workgroup.
+__device__ __forceinline__ void potrf64(double *A, int64_t n, int64_t k0)
+{
+    __shared__ double colb[2][kNb];
+    const int i = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    double a[kNb / 4];
+    double *row = A + (k0 + i) * n + k0;
+#pragma unroll
+    for (int t = 0; t < kNb / 4; ++t)
+        a[t] = 4 * t + w <= i ? row[4 * t + w] : 0.0;
+#pragma unroll
+    for (int j = 0; j < kNb; ++j) {
+        double *cb = colb[j & 1];
+        if (w == (j & 3)) {
+            // 1/sqrt of the pivot once, then products (no fp64 divide on the
+            // step's serial path)
+            const double p = bcast(a[j >> 2], j);
+            const double rs = rsqrt(p);
+            double v = a[j >> 2];
+            v = i == j ? p * rs : (i > j ? v * rs : v);
+            a[j >> 2] = v;
+            cb[i] = v;                             // L[i][j] for i >= j
+        }
+        __syncthreads();
+        const double lij = cb[i];
+#pragma unroll
+        for (int t = 0; t < kNb / 4; ++t)
+            if (4 * t + w > j)                     // uniform per wave
+                a[t] -= lij * cb[4 * t + w];
+    }
+#pragma unroll
+    for (int t = 0; t < kNb / 4; ++t)
+        if (4 * t + w <= i)
+            row[4 * t + w] = a[t];
+}
+
+__global__ __launch_bounds__(256) void k_potrf_diag(double *A, int64_t n, int64_t k0)
+{
+    potrf64(A, n, k0);
+}
+
+// ---------------------------------------------------------------------------
 // C[m][n] = alpha * sum_k A(m, k) B(k, n) + beta * C[m][n], for each batch z
 // (blockIdx.z) with A, B, C advanced by z * sA, z * sB, z * sC.
 // A(m, k) = TA ? A[k lda + m] : A[m lda + k];  B(k, n) = TB ? B[n ldb + k] : B[k ldb + n].
@@ -65,7 +125,7 @@ __device__ __forceinline__ void dgemm_fetch(const TAe *A, int64_t lda, const TBe
     }
 }
 
-template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER>
+template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false>
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha,
                                                const TAe *__restrict__ A, int64_t lda, int64_t sA,
                                                const TBe *__restrict__ B, int64_t ldb, int64_t sB, double beta,
@@ -128,9 +188,16 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
                     *c = beta == 0.0 ? prod : fma(beta, *c, prod);
                 }
             }
+    // POTRF: the workgroup of tile (0, 0) factors that tile once it is written
+    // (the next diagonal block of a blocked Cholesky, whose trailing update
+    // this is; the barrier makes the tile's stores visible to the workgroup).
+    if (POTRF && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+        __syncthreads();
+        potrf64(C, ldc, 0);
+    }
 }
 
-template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER>
+template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false>
 static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, int64_t lda, const TBe *B,
                   int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st, int64_t batch = 1,
                   int64_t sA = 0, int64_t sB = 0, int64_t sC = 0)
@@ -138,8 +205,8 @@ static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, i
     if (M <= 0 || N <= 0 || batch <= 0)
         return;
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
-    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER>), grid, dim3(256), 0, st, M, N, K, alpha, A, lda, sA,
-                       B, ldb, sB, beta, C, ldc, sC);
+    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER, POTRF>), grid, dim3(256), 0, st, M, N, K, alpha, A,
+                       lda, sA, B, ldb, sB, beta, C, ldc, sC);
 }
 
 // ---------------------------------------------------------------------------
@@ -185,54 +252,6 @@ __global__ __launch_bounds__(256) void k_fill0(double *a, int64_t total)
 {
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
         a[e] = 0.0;
-}
-
-// ---------------------------------------------------------------------------
-// Cholesky of the 64 x 64 diagonal block at (k0, k0), in place (lower): the
-// trailing updates of earlier panels are already applied. Four waves, one per
-// SIMD: lane i holds row i, wave w its columns l = 4t + w (t < 16). Step j:
-// the wave owning column j forms L[i][j] (the pivot's square root broadcast
-// from lane j) and publishes the column through LDS (double-buffered, so one
-// barrier per step suffices); every wave then removes L[i][j] L[l][j] from
-// its later columns. Entries above the diagonal are carried as scratch and
-// never written back.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ double bcast(double v, int src);
-
-__global__ __launch_bounds__(256) void k_potrf_diag(double *A, int64_t n, int64_t k0)
-{
-    __shared__ double colb[2][kNb];
-    const int i = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    double a[kNb / 4];
-    double *row = A + (k0 + i) * n + k0;
-#pragma unroll
-    for (int t = 0; t < kNb / 4; ++t)
-        a[t] = 4 * t + w <= i ? row[4 * t + w] : 0.0;
-#pragma unroll
-    for (int j = 0; j < kNb; ++j) {
-        double *cb = colb[j & 1];
-        if (w == (j & 3)) {
-            // 1/sqrt of the pivot once, then products (no fp64 divide on the
-            // step's serial path)
-            const double p = bcast(a[j >> 2], j);
-            const double rs = rsqrt(p);
-            double v = a[j >> 2];
-            v = i == j ? p * rs : (i > j ? v * rs : v);
-            a[j >> 2] = v;
-            cb[i] = v;                             // L[i][j] for i >= j
-        }
-        __syncthreads();
-        const double lij = cb[i];
-#pragma unroll
-        for (int t = 0; t < kNb / 4; ++t)
-            if (4 * t + w > j)                     // uniform per wave
-                a[t] -= lij * cb[4 * t + w];
-    }
-#pragma unroll
-    for (int t = 0; t < kNb / 4; ++t)
-        if (4 * t + w <= i)
-            row[4 * t + w] = a[t];
 }
 
 // Rows below the diagonal block: A[r][k0..k0+63] <- A[r][k0..] L_kk^-T. One
@@ -293,13 +312,6 @@ __global__ __launch_bounds__(64) void k_trtri_diag(const double *L, double *Li, 
 // One block of 128 columns [b, b + 128) for one row per wave. Lane l owns the
 // row's columns b + l and b + 64 + l.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double bcast(double v, int src)
-{
-    const long long u = __double_as_longlong(v);
-    const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffffLL), src);
-    const int hi = __builtin_amdgcn_readlane((int)(u >> 32), src);
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
 
 __device__ __forceinline__ double wave_max(double v)
 {
@@ -462,18 +474,19 @@ hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws,
     double *Lr = ws;                       // J H J, then (lower part) its Cholesky factor
     double *T = ws + total;                // products of the inverse's doubling steps (n*n/4)
     hipLaunchKernelGGL(k_reverse_copy, dim3(stream_blocks(total)), dim3(256), 0, st, H, Lr, total);
+    // The first diagonal block on its own; every later one is factored by the
+    // workgroup of the trailing update that writes it (POTRF).
     const int64_t nb = n / kNb;
-    for (int64_t k = 0; k < nb; ++k) {
+    hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, st, Lr, n, (int64_t)0);
+    for (int64_t k = 0; k + 1 < nb; ++k) {
         const int64_t k0 = k * kNb, rest = n - k0 - kNb;
-        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, st, Lr, n, k0);
-        if (rest > 0) {
-            hipLaunchKernelGGL(k_trsm_panel, dim3((unsigned)((rest + kTrsmRows - 1) / kTrsmRows)),
-                               dim3(kTrsmRows * 64), 0, st, Lr, n, k0);
-            // trailing lower triangle -= P P^T, P = the panel below the diagonal block
-            const double *P = Lr + (k0 + kNb) * n + k0;
-            dgemm<double, double, false, true, true>(rest, rest, kNb, -1.0, P, n, P, n, 1.0,
-                                                     Lr + (k0 + kNb) * n + k0 + kNb, n, st);
-        }
+        hipLaunchKernelGGL(k_trsm_panel, dim3((unsigned)((rest + kTrsmRows - 1) / kTrsmRows)),
+                           dim3(kTrsmRows * 64), 0, st, Lr, n, k0);
+        // trailing lower triangle -= P P^T, P = the panel below the diagonal
+        // block; then the next diagonal block is factored in place
+        const double *P = Lr + (k0 + kNb) * n + k0;
+        dgemm<double, double, false, true, true, true>(rest, rest, kNb, -1.0, P, n, P, n, 1.0,
+                                                       Lr + (k0 + kNb) * n + k0 + kNb, n, st);
     }
     // Li = L^-1 in U's buffer, bottom up: invert the 64 x 64 diagonal blocks,
     // then, with the inverses of every aligned run of s blocks known, combine
