@@ -101,80 +101,102 @@ __global__ __launch_bounds__(256) void k_potrf_diag(double *A, int64_t n, int64_
 // (blockIdx.z) with A, B, C advanced by z * sA, z * sB, z * sC.
 // A(m, k) = TA ? A[k lda + m] : A[m lda + k];  B(k, n) = TB ? B[n ldb + k] : B[k ldb + n].
 // LOWER: tiles entirely above the diagonal are skipped (only the lower
-// triangle of C is wanted). Block: 64 x 64 of C, 4 waves of 32 x 32; k in
-// steps of 16 through LDS (padded rows), the next step's elements loaded into
-// registers while the current one is multiplied; out-of-range elements load
-// as 0.
+// triangle of C is wanted). ACCC (alpha = -1, beta = 1 only): C -= A B with
+// the matrix cores accumulating onto C's own values, read into the
+// accumulators at the start (A's elements negated as they are staged, which
+// is exact); the epilogue then only stores. Block: 32 MI x 64 of C, 4 waves
+// of 16 MI x 32; k in steps of 16 through LDS (padded rows), the next step's
+// elements loaded into registers while the current one is multiplied;
+// out-of-range elements load as 0.
 // ---------------------------------------------------------------------------
-template <typename TAe, typename TBe, bool TA, bool TB>
+template <typename TAe, typename TBe, bool TA, bool TB, int MI>
 __device__ __forceinline__ void dgemm_fetch(const TAe *A, int64_t lda, const TBe *B, int64_t ldb, int64_t M,
                                             int64_t N, int64_t K, int64_t m0, int64_t n0, int64_t k0, int tid,
-                                            double (&ra)[4], double (&rb)[4])
+                                            double (&ra)[2 * MI], double (&rb)[4])
 {
+    constexpr int BM = 32 * MI;
+#pragma unroll
+    for (int q = 0; q < 2 * MI; ++q) {
+        const int e = q * 256 + tid;
+        int mm, kk;
+        if (TA) { mm = e % BM; kk = e / BM; } else { kk = e & 15; mm = e >> 4; }
+        const int64_t m = m0 + mm, k = k0 + kk;
+        ra[q] = (m < M && k < K) ? static_cast<double>(TA ? A[k * lda + m] : A[m * lda + k]) : 0.0;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = q * 256 + tid;
-        int mm, kk;
-        if (TA) { mm = e & 63; kk = e >> 6; } else { kk = e & 15; mm = e >> 4; }
-        const int64_t m = m0 + mm, k = k0 + kk;
-        ra[q] = (m < M && k < K) ? static_cast<double>(TA ? A[k * lda + m] : A[m * lda + k]) : 0.0;
-        int nn;
+        int nn, kk;
         if (TB) { kk = e & 15; nn = e >> 4; } else { nn = e & 63; kk = e >> 6; }
         const int64_t n = n0 + nn, k2 = k0 + kk;
         rb[q] = (n < N && k2 < K) ? static_cast<double>(TB ? B[n * ldb + k2] : B[k2 * ldb + n]) : 0.0;
     }
 }
 
-template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false>
+template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false, int MI = 2,
+          bool ACCC = false>
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha,
                                                const TAe *__restrict__ A, int64_t lda, int64_t sA,
                                                const TBe *__restrict__ B, int64_t ldb, int64_t sB, double beta,
                                                double *__restrict__ C, int64_t ldc, int64_t sC)
 {
-    __shared__ double As[16][65];
+    constexpr int BM = 32 * MI;
+    __shared__ double As[16][BM + 1];
     __shared__ double Bs[16][65];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
-    if (LOWER && n0 > m0 + 63)
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * 64;
+    if (LOWER && n0 > m0 + BM - 1)
         return;                                    // uniform for the block, before any barrier
     A += (int64_t)blockIdx.z * sA;
     B += (int64_t)blockIdx.z * sB;
     C += (int64_t)blockIdx.z * sC;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-    f64x4 acc[2][2];
+    const int wm = (wave >> 1) * 16 * MI, wn = (wave & 1) * 32;
+    f64x4 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-    double ra[4], rb[4];
-    dgemm_fetch<TAe, TBe, TA, TB>(A, lda, B, ldb, M, N, K, m0, n0, 0, tid, ra, rb);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm + i * 16 + (lane >> 4) + 4 * r;
+                const int64_t n = n0 + wn + j * 16 + (lane & 15);
+                acc[i][j][r] = (ACCC && m < M && n < N) ? C[m * ldc + n] : 0.0;
+            }
+    double ra[2 * MI], rb[4];
+    dgemm_fetch<TAe, TBe, TA, TB, MI>(A, lda, B, ldb, M, N, K, m0, n0, 0, tid, ra, rb);
     for (int64_t k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+        for (int q = 0; q < 2 * MI; ++q) {
+            const int e = q * 256 + tid;
+            const double v = ACCC ? -ra[q] : ra[q];
+            if (TA) As[e / BM][e % BM] = v; else As[e & 15][e >> 4] = v;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = q * 256 + tid;
-            if (TA) As[e >> 6][e & 63] = ra[q]; else As[e & 15][e >> 4] = ra[q];
             if (TB) Bs[e & 15][e >> 4] = rb[q]; else Bs[e >> 6][e & 63] = rb[q];
         }
         __syncthreads();
         if (k0 + 16 < K)
-            dgemm_fetch<TAe, TBe, TA, TB>(A, lda, B, ldb, M, N, K, m0, n0, k0 + 16, tid, ra, rb);
+            dgemm_fetch<TAe, TBe, TA, TB, MI>(A, lda, B, ldb, M, N, K, m0, n0, k0 + 16, tid, ra, rb);
 #pragma unroll
         for (int kk = 0; kk < 16; kk += 4) {
+            double bv[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int j = 0; j < 2; ++j)
+                bv[j] = Bs[kk + (lane >> 4)][wn + j * 16 + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
                 const double a = As[kk + (lane >> 4)][wm + i * 16 + (lane & 15)];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const double b = Bs[kk + (lane >> 4)][wn + j * 16 + (lane & 15)];
-                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[i][j], 0, 0, 0);
-                }
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv[j], acc[i][j], 0, 0, 0);
             }
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -184,8 +206,12 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
                 const int64_t n = n0 + wn + j * 16 + (lane & 15);
                 if (m < M && n < N) {
                     double *c = C + m * ldc + n;
-                    const double prod = alpha * acc[i][j][r];
-                    *c = beta == 0.0 ? prod : fma(beta, *c, prod);
+                    if (ACCC) {
+                        *c = acc[i][j][r];
+                    } else {
+                        const double prod = alpha * acc[i][j][r];
+                        *c = beta == 0.0 ? prod : fma(beta, *c, prod);
+                    }
                 }
             }
     // POTRF: the workgroup of tile (0, 0) factors that tile once it is written
@@ -197,15 +223,16 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     }
 }
 
-template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false>
+template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false, int MI = 2,
+          bool ACCC = false>
 static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, int64_t lda, const TBe *B,
                   int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st, int64_t batch = 1,
                   int64_t sA = 0, int64_t sB = 0, int64_t sC = 0)
 {
     if (M <= 0 || N <= 0 || batch <= 0)
         return;
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
-    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER, POTRF>), grid, dim3(256), 0, st, M, N, K, alpha, A,
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 32 * MI - 1) / (32 * MI)), (unsigned)batch);
+    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER, POTRF, MI, ACCC>), grid, dim3(256), 0, st, M, N, K, alpha, A,
                        lda, sA, B, ldb, sB, beta, C, ldc, sC);
 }
 
@@ -309,133 +336,162 @@ __global__ __launch_bounds__(64) void k_trtri_diag(const double *L, double *Li, 
 }
 
 // ---------------------------------------------------------------------------
-// One block of 128 columns [b, b + 128) for one row per wave. Lane l owns the
-// row's columns b + l and b + 64 + l.
+// One block of 128 columns [b, b + 128). A wave holds four rows, 16 lanes per
+// row; lane c of a row owns the row's columns b + c + 16 k (k < 8) in
+// registers. Column b + 16 k0 + c0 is quantised by lane c0 of each row (its
+// element k0); one shuffle hands its scaled error to the row's other lanes,
+// which subtract err * U[j][col] from their own columns. U's block sits in LDS
+// with its lower triangle and diagonal zeroed, so every lane updates all of
+// its columns not yet passed without a mask (err * 0 leaves a weight exact).
 // ---------------------------------------------------------------------------
+constexpr int kRowsPerGroup = 16;   // rows per workgroup of the column loop (4 waves)
+constexpr int kColRowLanes = 16;    // lanes per row
+constexpr int kColPerLane = kCol / kColRowLanes;   // 8
 
-__device__ __forceinline__ double wave_max(double v)
-{
-    for (int off = 32; off > 0; off >>= 1)
-        v = fmax(v, __shfl_xor(v, off));
-    return v;
-}
-__device__ __forceinline__ double wave_min(double v)
-{
-    for (int off = 32; off > 0; off >>= 1)
-        v = fmin(v, __shfl_xor(v, off));
-    return v;
-}
-
-constexpr int kRowsPerGroup = 16;   // rows (waves) per workgroup of the column loop
-
-__global__ __launch_bounds__(kRowsPerGroup * 64) void k_gptq_block(double *__restrict__ Wc,
+template <bool ASYM>
+__global__ __launch_bounds__(kRowsPerGroup * 16) void k_gptq_block(double *__restrict__ Wc,
                                                                     const double *__restrict__ U, int64_t out,
                                                                     int64_t in, int64_t b, int bits, int group,
-                                                                    int mode, double *__restrict__ E,
+                                                                    double *__restrict__ E,
                                                                     uint32_t *__restrict__ qweight,
                                                                     float *__restrict__ scales,
                                                                     uint8_t *__restrict__ zeros)
 {
-    // U[b : b + 128][b : b + 128] for every row of the workgroup (128 KB)
-    __shared__ double Us[kCol][kCol];
+    // Up[j][p][c] = {U[b + j][b + c + 32 p], U[b + j][b + c + 32 p + 16]} (strict upper part only):
+    // a row's 16 lanes read 256 contiguous bytes per pair of their columns
+    __shared__ double2 Up[kCol][kColPerLane / 2][kColRowLanes];
     __shared__ double rdiag[kCol];       // 1 / U[j][j]: the error's scaling without a division per column
-    for (int e = threadIdx.x; e < kCol * kCol; e += kRowsPerGroup * 64)
-        Us[e / kCol][e % kCol] = U[(b + e / kCol) * in + b + e % kCol];
-    __syncthreads();
+    __shared__ uint8_t cbuf[kRowsPerGroup][kCol];
+    for (int e = threadIdx.x; e < kCol * kCol / 2; e += kRowsPerGroup * 16) {
+        const int j = e >> 6, p = (e >> 4) & 3, c = e & 15;
+        const int c0 = c + 32 * p, c1 = c0 + 16;
+        const double *ur = U + (b + j) * in + b;
+        Up[j][p][c] = double2{c0 > j ? ur[c0] : 0.0, c1 > j ? ur[c1] : 0.0};
+    }
     if (threadIdx.x < kCol)
-        rdiag[threadIdx.x] = 1.0 / Us[threadIdx.x][threadIdx.x];
+        rdiag[threadIdx.x] = 1.0 / U[(b + threadIdx.x) * in + b + threadIdx.x];
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    const int r16 = (threadIdx.x >> 4);            // row within the workgroup
+    const int64_t o = (int64_t)blockIdx.x * kRowsPerGroup + r16;
+    const bool live = o < out;
+    double w[kColPerLane], e[kColPerLane];
+    uint32_t code[kColPerLane];
+    const double *row = Wc + (live ? o : 0) * in + b;
+#pragma unroll
+    for (int k = 0; k < kColPerLane; ++k) {
+        w[k] = live ? row[c + 16 * k] : 0.0;
+        e[k] = 0.0;
+        code[k] = 0;
+    }
     __syncthreads();
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t o = (int64_t)blockIdx.x * kRowsPerGroup + wv;
-    if (o >= out)
-        return;                                    // whole wave; no barrier below
-    double *row = Wc + o * in + b;
-    double w0 = row[lane], w1 = row[64 + lane];
-    double e0 = 0.0, e1 = 0.0;
-    uint32_t c0 = 0, c1 = 0;
     const double maxq = (double)((1 << bits) - 1);
     const double L = (double)((1 << (bits - 1)) - 1);
     const int64_t ng = in / group;
     double scale = 1.0, zero = 0.0, rscale = 1.0;
-    for (int jj = 0; jj < kCol; ++jj) {
-        const int64_t j = b + jj;
-        if (jj % group == 0) {
-            // group parameters on the current (corrected) weights of [j, j + group)
-            const bool in0 = lane >= jj && lane < jj + group;
-            const bool in1 = 64 + lane >= jj && 64 + lane < jj + group;
+#pragma unroll
+    for (int k0 = 0; k0 < kColPerLane; ++k0) {
+        if ((16 * k0) % group == 0) {
+            // group parameters on the current (corrected) weights of the row's
+            // columns [b + 16 k0, b + 16 k0 + group); groups are 32, 64 or 128
+            // wide, so a group starts at a multiple of 16
+            const int kend = k0 + group / 16;
             double s64;
-            if (mode == AWQ_ASYM) {
+            if (ASYM) {
                 double lo = 0.0, hi = 0.0;     // the range always contains 0
-                if (in0) { lo = fmin(lo, w0); hi = fmax(hi, w0); }
-                if (in1) { lo = fmin(lo, w1); hi = fmax(hi, w1); }
-                lo = wave_min(lo);
-                hi = wave_max(hi);
+#pragma unroll
+                for (int k = k0; k < kColPerLane; ++k)
+                    if (k < kend) { lo = fmin(lo, w[k]); hi = fmax(hi, w[k]); }
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1) {
+                    lo = fmin(lo, __shfl_xor(lo, off));
+                    hi = fmax(hi, __shfl_xor(hi, off));
+                }
                 s64 = fmax((hi - lo) / maxq, 1e-8);
                 scale = (double)(float)s64;
                 zero = rint(-lo / scale);
-                rscale = 1.0 / scale;
             } else {
                 double a = 0.0;
-                if (in0) a = fmax(a, fabs(w0));
-                if (in1) a = fmax(a, fabs(w1));
-                a = wave_max(a);
+#pragma unroll
+                for (int k = k0; k < kColPerLane; ++k)
+                    if (k < kend) a = fmax(a, fabs(w[k]));
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1)
+                    a = fmax(a, __shfl_xor(a, off));
                 s64 = fmax(a / L, 1e-8);
                 scale = (double)(float)s64;
                 zero = (double)(1 << (bits - 1));
-                rscale = 1.0 / scale;
             }
-            if (lane == 0) {
-                scales[o * ng + j / group] = (float)scale;
-                zeros[o * ng + j / group] = (uint8_t)(int)zero;
+            rscale = 1.0 / scale;
+            if (live && c == 0) {
+                const int64_t gi = o * ng + (b + 16 * k0) / group;
+                scales[gi] = (float)scale;
+                zeros[gi] = (uint8_t)(int)zero;
             }
         }
-        const int owner = jj & 63;
-        const double w = bcast(jj < 64 ? w0 : w1, owner);
-        // rint(w / scale) off the division's latency: t = w * (1/scale) is
-        // within 3 ulp of the quotient, so the two round to the same integer
-        // unless t lies within 1e-9 of a half-integer (true for |t| < 2^20;
-        // larger quotients are clamped to the code range either way); there,
-        // and at exact ties, the quotient itself decides
-        double r = rint(w * rscale);
-        if (fabs(fabs(w * rscale - r) - 0.5) < 1e-9)
-            r = rint(w / scale);
-        double q, wq;
-        uint32_t code;
-        if (mode == AWQ_ASYM) {
-            q = fmin(fmax(r + zero, 0.0), maxq);
-            wq = scale * (q - zero);
-            code = (uint32_t)(int)q;
-        } else {
-            q = fmin(fmax(r, -L - 1.0), L);
-            wq = scale * q;
-            code = (uint32_t)((int)q + (1 << (bits - 1)));
+#pragma unroll 1
+        for (int c0 = 0; c0 < kColRowLanes; ++c0) {
+            const int jj = 16 * k0 + c0;
+            double2 u[kColPerLane / 2];
+#pragma unroll
+            for (int p = k0 / 2; p < kColPerLane / 2; ++p)
+                u[p] = Up[jj][p][c];
+            const double rd = rdiag[jj];
+            // every lane runs the step on its element k0; lane c0's result is the row's
+            const double wv = w[k0];
+            // rint(w / scale) off the division's latency: t = w * (1/scale) is
+            // within 3 ulp of the quotient, so the two round to the same integer
+            // unless t lies within 1e-9 of a half-integer (true for |t| < 2^20;
+            // larger quotients are clamped to the code range either way); there,
+            // and at exact ties, the quotient itself decides
+            const double t = wv * rscale;
+            double r = rint(t);
+            if (fabs(fabs(t - r) - 0.5) < 1e-9)
+                r = rint(wv / scale);
+            double q, wq;
+            uint32_t cd;
+            if (ASYM) {
+                q = fmin(fmax(r + zero, 0.0), maxq);
+                wq = scale * (q - zero);
+                cd = (uint32_t)(int)q;
+            } else {
+                q = fmin(fmax(r, -L - 1.0), L);
+                wq = scale * q;
+                cd = (uint32_t)((int)q + (1 << (bits - 1)));
+            }
+            const double mine = (wv - wq) * rd;
+            const double err = __shfl(mine, (lane & 48) | c0);
+            if (c == c0) {
+                e[k0] = mine;
+                code[k0] = cd;
+            }
+#pragma unroll
+            for (int k = k0; k < kColPerLane; ++k)
+                w[k] -= err * (k & 1 ? u[k / 2].y : u[k / 2].x);
         }
-        const double err = (w - wq) * rdiag[jj];
-        if (lane == owner) {
-            if (jj < 64) { e0 = err; c0 = code; } else { e1 = err; c1 = code; }
-        }
-        if (lane > jj)
-            w0 -= err * Us[jj][lane];
-        if (64 + lane > jj)
-            w1 -= err * Us[jj][64 + lane];
     }
-    E[o * kCol + lane] = e0;
-    E[o * kCol + 64 + lane] = e1;
-    // the block's 128 codes fill exactly 4 * bits words of the row's stream:
-    // every code is broadcast in turn and each of the first 4 * bits lanes
-    // keeps the bits that fall into its word
-    uint32_t word = 0;
-    for (int i = 0; i < kCol; ++i) {
-        const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)(i < 64 ? c0 : c1), i & 63);
-        const int sh = i * bits - 32 * lane;
-        if (sh >= 0 && sh < 32)
-            word |= c << sh;
-        else if (sh < 0 && sh > -bits)
-            word |= c >> -sh;
+    if (live) {
+        double *er = E + o * kCol;
+#pragma unroll
+        for (int k = 0; k < kColPerLane; ++k)
+            er[c + 16 * k] = e[k];
     }
-    if (lane < 4 * bits) {
+#pragma unroll
+    for (int k = 0; k < kColPerLane; ++k)
+        cbuf[r16][c + 16 * k] = (uint8_t)code[k];
+    __syncthreads();
+    // the block's 128 codes fill exactly 4 * bits words of the row's stream
+    if (live) {
         const int64_t wpr = in * bits / 32;
-        qweight[o * wpr + (b * bits) / 32 + lane] = word;
+        for (int wd = c; wd < 4 * bits; wd += kColRowLanes) {
+            uint32_t word = 0;
+            const int first = (32 * wd) / bits, last = (32 * wd + 31) / bits;
+            for (int i = first; i <= last; ++i) {
+                const uint32_t cv = cbuf[r16][i];
+                const int sh = i * bits - 32 * wd;
+                word |= sh >= 0 ? cv << sh : cv >> -sh;
+            }
+            qweight[o * wpr + (b * bits) / 32 + wd] = word;
+        }
     }
 }
 
@@ -485,7 +541,7 @@ hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws,
         // trailing lower triangle -= P P^T, P = the panel below the diagonal
         // block; then the next diagonal block is factored in place
         const double *P = Lr + (k0 + kNb) * n + k0;
-        dgemm<double, double, false, true, true, true>(rest, rest, kNb, -1.0, P, n, P, n, 1.0,
+        dgemm<double, double, false, true, true, true, 2, true>(rest, rest, kNb, -1.0, P, n, P, n, 1.0,
                                                        Lr + (k0 + kNb) * n + k0 + kNb, n, st);
     }
     // Li = L^-1 in U's buffer, bottom up: invert the 64 x 64 diagonal blocks,
@@ -546,13 +602,15 @@ hipError_t launch_gptq_quantize(const void *W, int dtype, int64_t out, int64_t i
         break;
     }
     for (int64_t b = 0; b < in; b += kCol) {
-        hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)((out + kRowsPerGroup - 1) / kRowsPerGroup)),
-                           dim3(kRowsPerGroup * 64), 0, st, Wc, U, out, in, b, bits, group, mode, E, qweight,
+        hipLaunchKernelGGL(mode == AWQ_ASYM ? k_gptq_block<true> : k_gptq_block<false>,
+                           dim3((unsigned)((out + kRowsPerGroup - 1) / kRowsPerGroup)),
+                           dim3(kRowsPerGroup * kColRowLanes), 0, st, Wc, U, out, in, b, bits, group, E, qweight,
                            scales, zeros);
         const int64_t rest = in - b - kCol;
         if (rest > 0)   // later columns -= E U[b : b + 128][b + 128 :]
-            dgemm<double, double, false, false, false>(out, rest, kCol, -1.0, E, kCol, U + b * in + b + kCol, in,
-                                                       1.0, Wc + b + kCol, in, st);
+            dgemm<double, double, false, false, false, false, 2, true>(out, rest, kCol, -1.0, E, kCol,
+                                                                      U + b * in + b + kCol, in, 1.0, Wc + b + kCol,
+                                                                      in, st);
     }
     return hipGetLastError();
 }
