@@ -93,6 +93,11 @@ QCASES = [
     ("bf16", "asym", 3, 64, 20, 256, 500),
     ("f32", "sym", 8, 32, 9, 128, 64),
     ("bf16", "asym", 2, 32, 16, 512, 600),
+    # odd widths: codes cross 32-bit words, and 5-7 bits give 20-28 words per
+    # 128-column block, more than the 16 lanes of a row in the column loop
+    ("f16", "sym", 5, 64, 33, 384, 300),
+    ("f16", "asym", 6, 32, 18, 640, 700),
+    ("bf16", "asym", 7, 128, 50, 256, 400),
 ]
 
 
