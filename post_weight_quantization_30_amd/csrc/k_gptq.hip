@@ -18,11 +18,17 @@
 //    factor L of J H J gives H = (J L J)(J L J)^T with J L J upper, hence
 //    H^-1 = (J L^-1 J)^T (J L^-1 J) and, by uniqueness, U = J L^-1 J: one
 //    blocked Cholesky and one blocked triangular inverse (panels of 64);
-//  - the column loop in blocks of 128 columns: one wave per row takes the
-//    block's columns one at a time (lanes own two columns each; the column's
-//    value is broadcast, the quantizer runs uniformly, every lane updates its
-//    later columns), then one GEMM applies the block's 128 errors to all later
-//    columns (the page's "batch the updates in blocks of 128").
+//  - the blocked Cholesky factors each 64 x 64 diagonal block inside the
+//    trailing-update GEMM that produces it (its tile-(0, 0) workgroup);
+//  - the column loop in blocks of 128 columns: four rows per wave, 16 lanes
+//    per row, each lane owning 8 of the block's columns; a column is
+//    quantised in every row at once by its owner lanes and the scaled error
+//    is shuffled to the row's other lanes, which update their later columns;
+//    then one GEMM applies the block's 128 errors to all later columns (the
+//    page's "batch the updates in blocks of 128").
+//  The serial parts (the diagonal blocks, the panel solves, the column loop)
+//  are bound by the latency of their chains of dependent fp64 operations,
+//  about 15 ns each on one wave.
 #include "awq_internal.h"
 
 #include <math.h>
