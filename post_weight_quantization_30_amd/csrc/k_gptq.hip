@@ -450,21 +450,26 @@ __global__ __launch_bounds__(kRowsPerGroup * 16) void k_gptq_block(double *__res
             // larger quotients are clamped to the code range either way); there,
             // and at exact ties, the quotient itself decides
             const double t = wv * rscale;
-            double r = rint(t);
-            if (fabs(fabs(t - r) - 0.5) < 1e-9)
-                r = rint(wv / scale);
-            double q, wq;
+            // the step from rint(t); the near-tie test runs beside it and
+            // its rare redo comes last, off the step's dependent chain
+            auto step = [&](double r, uint32_t &cd) {
+                double q, wq;
+                if (ASYM) {
+                    q = fmin(fmax(r + zero, 0.0), maxq);
+                    wq = scale * (q - zero);
+                    cd = (uint32_t)(int)q;
+                } else {
+                    q = fmin(fmax(r, -L - 1.0), L);
+                    wq = scale * q;
+                    cd = (uint32_t)((int)q + (1 << (bits - 1)));
+                }
+                return (wv - wq) * rd;
+            };
+            const double r0 = rint(t);
             uint32_t cd;
-            if (ASYM) {
-                q = fmin(fmax(r + zero, 0.0), maxq);
-                wq = scale * (q - zero);
-                cd = (uint32_t)(int)q;
-            } else {
-                q = fmin(fmax(r, -L - 1.0), L);
-                wq = scale * q;
-                cd = (uint32_t)((int)q + (1 << (bits - 1)));
-            }
-            const double mine = (wv - wq) * rd;
+            double mine = step(r0, cd);
+            if (fabs(fabs(t - r0) - 0.5) < 1e-9)
+                mine = step(rint(wv / scale), cd);
             const double err = __shfl(mine, (lane & 48) | c0);
             if (c == c0) {
                 e[k0] = mine;
