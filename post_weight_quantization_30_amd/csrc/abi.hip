@@ -378,7 +378,9 @@ int awq_quantize_pack_clip(const void *W, int dtype, int64_t out, int64_t in, co
         return AWQ_ERR_INVALID_ARG;
     if (!pack_group_ok(group) || !aligned16(W) || !aligned16(s))
         return AWQ_ERR_UNSUPPORTED;
-    if ((out * (in / 32) + 255) / 256 > (int64_t)0x7fffffff)
+    // grid: 4-row blocks x 2048-column tiles
+    const int64_t row_blocks = (out + 3) / 4, tiles = (in / 32 + 63) / 64;
+    if (tiles > (int64_t)0x7fffffff / row_blocks)
         return AWQ_ERR_UNSUPPORTED;
     return hip_status(awq::launch_pack(W, dtype, out, in, s, clip, bits, group, mode, qweight,
                                        scales, zeros, (hipStream_t)stream));

@@ -20,9 +20,11 @@
 // Layout: one lane owns 32 consecutive columns of one row. 32 codes of b bits
 // fill exactly b 32-bit words, so a lane writes whole words of the row's
 // little-endian bit stream with no neighbour; a group of G columns spans G/32
-// adjacent lanes, whose max/min are combined with xor shuffles. Loads and
-// stores of a wave are contiguous. HBM bound: read W (2 or 4 B per weight),
-// write b/8 B per weight plus 5 B per group.
+// adjacent lanes, whose max/min are combined with xor shuffles. A wave takes
+// 2048 consecutive columns of one row and four waves take four rows of the
+// same columns, whose scale factors are read from HBM once per block. Loads
+// and stores of a wave are contiguous. HBM bound: read W (2 or 4 B per
+// weight), write b/8 B per weight plus 5 B per group.
 #include "awq_internal.h"
 
 #include <float.h>
@@ -100,28 +102,51 @@ __device__ __forceinline__ void codes(const float (&v)[32], float scale, float l
     }
 }
 
+// Block: kPackRows rows (one wave each) x kPackChunks 32-column chunks (2048
+// columns, a multiple of every group); the tile's 2048 scale factors are
+// staged once in LDS and shared by its rows.
+constexpr int kPackRows = 4;
+constexpr int kPackChunks = 64;
+
 template <typename T, int BITS, bool CLIP>
-__global__ __launch_bounds__(256) void k_quantize_pack(const T *__restrict__ W, int64_t out,
-                                                        int64_t in, const float *__restrict__ s,
-                                                        const float *__restrict__ clip,
-                                                        int lanes_per_group, int mode,
-                                                        uint32_t *__restrict__ qweight,
-                                                        float *__restrict__ scales,
-                                                        uint8_t *__restrict__ zeros)
+__global__ __launch_bounds__(kPackRows * 64) void k_quantize_pack(const T *__restrict__ W, int64_t out,
+                                                                  int64_t in, const float *__restrict__ s,
+                                                                  const float *__restrict__ clip,
+                                                                  int lanes_per_group, int mode,
+                                                                  uint32_t *__restrict__ qweight,
+                                                                  float *__restrict__ scales,
+                                                                  uint8_t *__restrict__ zeros)
 {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    // sl[i][l] = s[c0 + 32 l + 4 i .. + 3]: lane l's 32 factors as eight
+    // 16-byte reads at consecutive addresses across the lanes
+    __shared__ f32x4v sl[8][kPackChunks];
     const int64_t chunks = in / 32;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool active = gid < out * chunks;
-    const int64_t row = active ? gid / chunks : 0;
-    const int64_t ch = active ? gid % chunks : 0;
+    const int64_t tiles = (chunks + kPackChunks - 1) / kPackChunks;
+    const int64_t rblk = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    {
+        const int l = threadIdx.x >> 2, part = threadIdx.x & 3;   // 8 factors each
+        const int64_t col = (tile * kPackChunks + l) * 32 + part * 8;
+        f32x8 s8 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (col < in)                              // in % 32 == 0: all 8 are in range
+            s8 = *reinterpret_cast<const f32x8 *>(s + col);
+        sl[2 * part][l] = f32x4v{s8[0], s8[1], s8[2], s8[3]};
+        sl[2 * part + 1][l] = f32x4v{s8[4], s8[5], s8[6], s8[7]};
+    }
+    __syncthreads();
+    const int64_t row_raw = rblk * kPackRows + wave, ch_raw = tile * kPackChunks + lane;
+    const bool active = row_raw < out && ch_raw < chunks;
+    const int64_t row = active ? row_raw : 0;
+    const int64_t ch = active ? ch_raw : 0;
 
     float v[32];
     if (active) {
         const T *wp = W + row * in + ch * 32;
-        const float *sp = s + ch * 32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const f32x8 s8 = *reinterpret_cast<const f32x8 *>(sp + q * 8);
+            const f32x4v s_lo = sl[2 * q][lane], s_hi = sl[2 * q + 1][lane];
+            const f32x8 s8 = {s_lo[0], s_lo[1], s_lo[2], s_lo[3], s_hi[0], s_hi[1], s_hi[2], s_hi[3]};
             if constexpr (std::is_same<T, f16>::value) {
                 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
                 const u32x4 pr = __builtin_bit_cast(u32x4, load8(wp + q * 8));
@@ -214,10 +239,10 @@ static void pack_typed(const T *W, int64_t out, int64_t in, const float *s, cons
                        int bits, int lpg, int mode, uint32_t *qweight, float *scales,
                        uint8_t *zeros, hipStream_t st)
 {
-    const int64_t threads = out * (in / 32);
-    dim3 grid((unsigned)((threads + 255) / 256));
-#define AWQ_PACK_LAUNCH(B)                                                                   \
-    hipLaunchKernelGGL((k_quantize_pack<T, B, CLIP>), grid, dim3(256), 0, st, W, out, in, s, \
+    const int64_t tiles = (in / 32 + kPackChunks - 1) / kPackChunks;
+    dim3 grid((unsigned)(((out + kPackRows - 1) / kPackRows) * tiles));
+#define AWQ_PACK_LAUNCH(B)                                                                               \
+    hipLaunchKernelGGL((k_quantize_pack<T, B, CLIP>), grid, dim3(kPackRows * 64), 0, st, W, out, in, s, \
                        clip, lpg, mode, qweight, scales, zeros)
     switch (bits) {
     case 2: AWQ_PACK_LAUNCH(2); break;
