@@ -68,7 +68,8 @@ def check_search(mse_g, best_g, sbest_g, mse_o, best_o, stab_o, label=""):
 # statistics and s-table: bitwise
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("T,n_in", [(1, 32), (100, 256), (256, 4096), (333, 100), (64, 4098)])
+@pytest.mark.parametrize("T,n_in", [(1, 32), (100, 256), (256, 4096), (333, 100), (64, 4098),
+                                    (1024, 130), (1025, 70), (2000, 300), (4096, 96)])
 def test_act_stats_bitwise(awq, ref, dtype, T, n_in):
     say("act_stats", dtype, T, n_in)
     spec = synth.LayerSpec("s", 1, n_in, T, dtype, 4, 32, 2, "sym", 77 + T, outlier_n=min(3, n_in),
