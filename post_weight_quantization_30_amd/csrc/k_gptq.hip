@@ -140,7 +140,7 @@ __device__ __forceinline__ void dgemm_fetch(const TAe *A, int64_t lda, const TBe
 }
 
 template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false, int MI = 2,
-          bool ACCC = false>
+          bool ACCC = false, int TRI = 0>
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha,
                                                const TAe *__restrict__ A, int64_t lda, int64_t sA,
                                                const TBe *__restrict__ B, int64_t ldb, int64_t sB, double beta,
@@ -168,9 +168,15 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
                 const int64_t n = n0 + wn + j * 16 + (lane & 15);
                 acc[i][j][r] = (ACCC && m < M && n < N) ? C[m * ldc + n] : 0.0;
             }
+    // TRI: a triangular operand's exact zeros are skipped (their products
+    // add nothing): 1 = B lower (B(k, n) = 0 for k < n), 2 = A lower
+    // (A(m, k) = 0 for k > m). The tile's k-range shrinks to where both can
+    // be non-zero; the k-steps kept are the same, in the same order.
+    const int64_t kbeg = TRI == 1 ? (n0 / 16) * 16 : 0;
+    const int64_t kend = TRI == 2 ? (m0 + BM < K ? m0 + BM : K) : K;
     double ra[2 * MI], rb[4];
-    dgemm_fetch<TAe, TBe, TA, TB, MI>(A, lda, B, ldb, M, N, K, m0, n0, 0, tid, ra, rb);
-    for (int64_t k0 = 0; k0 < K; k0 += 16) {
+    dgemm_fetch<TAe, TBe, TA, TB, MI>(A, lda, B, ldb, M, N, K, m0, n0, kbeg, tid, ra, rb);
+    for (int64_t k0 = kbeg; k0 < kend; k0 += 16) {
 #pragma unroll
         for (int q = 0; q < 2 * MI; ++q) {
             const int e = q * 256 + tid;
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
             if (TB) Bs[e & 15][e >> 4] = rb[q]; else Bs[e >> 6][e & 63] = rb[q];
         }
         __syncthreads();
-        if (k0 + 16 < K)
+        if (k0 + 16 < kend)
             dgemm_fetch<TAe, TBe, TA, TB, MI>(A, lda, B, ldb, M, N, K, m0, n0, k0 + 16, tid, ra, rb);
 #pragma unroll
         for (int kk = 0; kk < 16; kk += 4) {
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
 }
 
 template <typename TAe, typename TBe, bool TA, bool TB, bool LOWER, bool POTRF = false, int MI = 2,
-          bool ACCC = false>
+          bool ACCC = false, int TRI = 0>
 static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, int64_t lda, const TBe *B,
                   int64_t ldb, double beta, double *C, int64_t ldc, hipStream_t st, int64_t batch = 1,
                   int64_t sA = 0, int64_t sB = 0, int64_t sC = 0)
@@ -238,7 +244,7 @@ static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, i
     if (M <= 0 || N <= 0 || batch <= 0)
         return;
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 32 * MI - 1) / (32 * MI)), (unsigned)batch);
-    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER, POTRF, MI, ACCC>), grid, dim3(256), 0, st, M, N, K, alpha, A,
+    hipLaunchKernelGGL((k_dgemm<TAe, TBe, TA, TB, LOWER, POTRF, MI, ACCC, TRI>), grid, dim3(256), 0, st, M, N, K, alpha, A,
                        lda, sA, B, ldb, sB, beta, C, ldc, sC);
 }
 
@@ -567,19 +573,23 @@ hipError_t launch_gptq_factor(const double *H, int64_t n, double *U, double *ws,
     hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, Lr, Li, n);
     for (int64_t s = 1; s < nb; s *= 2) {
         const int64_t S = s * kNb, full = nb / (2 * s), step = 2 * S * n + 2 * S;
+        // A^-1 and C^-1 are lower triangular (zeros above their diagonals)
         if (full > 0) {
-            dgemm<double, double, false, false, false>(S, S, S, 1.0, Lr + S * n, n, Li, n, 0.0, Tb, S, st, full,
-                                                       step, step, S * S);
-            dgemm<double, double, false, false, false>(S, S, S, -1.0, Li + S * n + S, n, Tb, S, 0.0, Li + S * n, n,
-                                                       st, full, step, S * S, step);
+            dgemm<double, double, false, false, false, false, 2, false, 1>(S, S, S, 1.0, Lr + S * n, n, Li, n, 0.0,
+                                                                         Tb, S, st, full, step, step, S * S);
+            dgemm<double, double, false, false, false, false, 2, false, 2>(S, S, S, -1.0, Li + S * n + S, n, Tb, S,
+                                                                         0.0, Li + S * n, n, st, full, step,
+                                                                         S * S, step);
         }
         const int64_t rem = nb - full * 2 * s;
         if (rem > s) {
             const int64_t base = full * 2 * S, S2 = (rem - s) * kNb;
-            dgemm<double, double, false, false, false>(S2, S, S, 1.0, Lr + (base + S) * n + base, n,
-                                                       Li + base * n + base, n, 0.0, Tb, S, st);
-            dgemm<double, double, false, false, false>(S2, S, S2, -1.0, Li + (base + S) * n + base + S, n, Tb, S,
-                                                       0.0, Li + (base + S) * n + base, n, st);
+            dgemm<double, double, false, false, false, false, 2, false, 1>(S2, S, S, 1.0, Lr + (base + S) * n + base,
+                                                                         n, Li + base * n + base, n, 0.0, Tb, S,
+                                                                         st);
+            dgemm<double, double, false, false, false, false, 2, false, 2>(S2, S, S2, -1.0,
+                                                                         Li + (base + S) * n + base + S, n, Tb, S,
+                                                                         0.0, Li + (base + S) * n + base, n, st);
         }
     }
     hipLaunchKernelGGL(k_reverse_inplace, dim3(stream_blocks(total / 2)), dim3(256), 0, st, U, total);
