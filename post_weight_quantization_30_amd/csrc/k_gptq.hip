@@ -249,6 +249,32 @@ static void dgemm(int64_t M, int64_t N, int64_t K, double alpha, const TAe *A, i
 }
 
 // ---------------------------------------------------------------------------
+// Upper triangle of a symmetric matrix from its lower one, a 64 x 64 tile per
+// block through LDS (coalesced reads of tile (J, I), coalesced writes of
+// tile (I, J)); tiles on and below the diagonal are left as they are.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_mirror_upper(double *H, int64_t n)
+{
+    const int64_t ti = blockIdx.y, tj = blockIdx.x;
+    if (tj <= ti)
+        return;                                    // whole block
+    __shared__ double t[64][65];
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int r = e >> 6, c = e & 63;          // element (tj*64 + r, ti*64 + c)
+        const int64_t gr = tj * 64 + r, gc = ti * 64 + c;
+        if (gr < n && gc < n)
+            t[r][c] = H[gr * n + gc];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int c = e >> 6, r = e & 63;          // element (ti*64 + c, tj*64 + r)
+        const int64_t gr = ti * 64 + c, gc = tj * 64 + r;
+        if (gr < n && gc < n)
+            H[gr * n + gc] = t[r][c];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dampening: H[i][i] += damp * mean(diag H). One block; fixed summation order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_damp(double *H, int64_t n, double damp)
@@ -518,8 +544,12 @@ __global__ __launch_bounds__(kRowsPerGroup * 16) void k_gptq_block(double *__res
 template <typename T>
 static void hessian_typed(const T *X, int64_t tokens, int64_t in, double *H, hipStream_t st)
 {
-    // H = 2 X^T X: A(m, k) = X[k][m] (TA), B(k, n) = X[k][n]
-    dgemm<T, T, true, false, false>(in, in, tokens, 2.0, X, in, X, in, 0.0, H, in, st);
+    // H = 2 X^T X: A(m, k) = X[k][m] (TA), B(k, n) = X[k][n]. Symmetric: the
+    // tiles on and below the diagonal, then the upper ones mirrored (element
+    // (j, i) is the same products summed in the same token order as (i, j))
+    dgemm<T, T, true, false, true>(in, in, tokens, 2.0, X, in, X, in, 0.0, H, in, st);
+    const unsigned tiles = (unsigned)((in + 63) / 64);
+    hipLaunchKernelGGL(k_mirror_upper, dim3(tiles, tiles), dim3(256), 0, st, H, in);
 }
 
 hipError_t launch_gptq_hessian(const void *X, int dtype, int64_t tokens, int64_t in, double damp, double *H,
