@@ -343,9 +343,12 @@ def gptq_measure(awq, torch, spec, W, X, xmag_mse, args, awq_pack=None):
         qa, sa, za, s_best = awq_pack
         X2s = (X2.float() / s_best[None, :]).to(X2.dtype).contiguous()
         held["awq"] = float(((awq.qgemm(X2s, qa, sa, za, spec.bits, spec.group, y_f32=True) - ref2) ** 2).mean())
-    flops = {"hessian": 2.0 * T * n_in * n_in,
-             "factor": 2.0 * (n_in ** 3) / 3 * 2,            # Cholesky + triangular inverse
-             "quantize": 2.0 * out * n_in * n_in / 2}        # compensation products
+    # algorithmic FLOPs: H is symmetric (one triangle, T in (in + 1)); a
+    # Cholesky factor and a triangular inverse take in^3 / 3 each; the
+    # compensation products sum out * (in - j) * 2 over the columns j
+    flops = {"hessian": 1.0 * T * n_in * (n_in + 1),
+             "factor": 2.0 * (n_in ** 3) / 3,
+             "quantize": 1.0 * out * n_in * n_in}
     tf = {s: flops[s] / (st[s] * 1e-3) / 1e12 for s in st}
     return {"ms": total, "stages_ms": st, "tflops": tf,
             "roofline": {"bound": "mfma", "kernel": "GPTQ quantize stage (k_dgemm f64 + k_gptq_block)",
