@@ -565,6 +565,243 @@ __global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf(const TX *__restrict_
         }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill with 32 x 32 x 16 MFMAs: one block = 64 tokens x 256 output rows
+// over all of K, wave w taking rows 32 w .. +31 for both 32-token tiles, so
+// every staged X fragment serves 32 rows (half the LDS reads per product of
+// the 16 x 16 tile above). A = X (lane l: token l % 32), B = the (code -
+// zero) operands (lane l: row l % 32), so a lane's 16 results all belong to
+// one output row and take one group scale. MFMA step s of a group covers
+// its 16 columns 16 s .. 16 s + 15, lanes 0-31 the first eight, lanes 32-63
+// the last eight: a step never straddles a group. The codes of each row and
+// group are staged with the 8-code units of the two lane halves made
+// contiguous (even units first, then odd ones).
+// ---------------------------------------------------------------------------
+constexpr int kP2M = 64, kP2N = 256, kP2K = 128;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename TX> struct QOp32;
+template <> struct QOp32<f16> {
+    static __device__ __forceinline__ f32x16 mfma(const f16x8 &a, const f16x8 &b, const f32x16 &c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct QOp32<bf16> {
+    static __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <int BITS>
+struct P2Stage {
+    static constexpr int XROW = kP2K * 2 + 16;                  // LDS bytes per token row (padded)
+    static constexpr int XB = kP2M * XROW;
+    static constexpr int CRB = kP2K * BITS / 8;                 // code bytes of one row in a chunk
+    static constexpr int CROW = CRB + 16;
+    static constexpr int CB = kP2N * CROW;
+    static constexpr int NGMAX = kP2K / 32;
+    static constexpr int BUF = XB + CB + kP2N * NGMAX * 4 + kP2N * NGMAX;
+    static constexpr int XCH = kP2M * kP2K * 2 / 16 / (kQWaves * 64);   // 16-byte X chunks per thread (2)
+    static constexpr int CCH = kP2N * CRB / 16 / (kQWaves * 64);        // 16-byte code chunks per thread
+    static constexpr int SZ = (kP2N * NGMAX + kQWaves * 64 - 1) / (kQWaves * 64);   // scales per thread
+};
+
+template <typename TX, int BITS, int G, bool YF32>
+__global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf32(const TX *__restrict__ X, int64_t M, int64_t in,
+                                                             const uint32_t *__restrict__ qweight,
+                                                             const float *__restrict__ scales,
+                                                             const uint8_t *__restrict__ zeros, int64_t out,
+                                                             void *__restrict__ Y)
+{
+    typedef P2Stage<BITS> S;
+    typedef typename QOp<TX>::vec vec;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int GPC = kP2K / G;               // groups per chunk
+    constexpr int STEPS = G / 16;               // 16-column MFMA steps per group
+    constexpr int GB = G * BITS / 8;            // code bytes of one group of one row
+    constexpr int UB = BITS;                    // bytes of one 8-code unit
+    constexpr int UPG = G / 8;                  // units per group
+    constexpr uint32_t cmask = (1u << BITS) - 1u;
+    constexpr bool kPairs = std::is_same<TX, f16>::value;
+    __shared__ __align__(16) uint8_t lds[2 * S::BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, kh = lane >> 5;
+    const int64_t m0 = (int64_t)blockIdx.y * kP2M, n0 = (int64_t)blockIdx.x * kP2N;
+    const int64_t ng = in / G, row_bytes = in * BITS / 8;
+    const int64_t chunks = in / kP2K;
+    const uint8_t *qbytes = reinterpret_cast<const uint8_t *>(qweight);
+
+    u32x4 xr[S::XCH], cr[S::CCH];
+    float sr[S::SZ];
+    uint8_t zr[S::SZ];
+    auto fetch = [&](int64_t kc) {
+#pragma unroll
+        for (int i = 0; i < S::XCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            int64_t m = m0 + ch / (kP2K * 2 / 16);
+            m = m < M ? m : M - 1;
+            xr[i] = *reinterpret_cast<const u32x4 *>(X + m * in + kc * kP2K + (ch % (kP2K * 2 / 16)) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < S::CCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            int64_t n = n0 + ch / (S::CRB / 16);
+            n = n < out ? n : out - 1;
+            cr[i] = *reinterpret_cast<const u32x4 *>(qbytes + n * row_bytes + kc * S::CRB + (ch % (S::CRB / 16)) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < S::SZ; ++i) {
+            const int e = tid + i * kQWaves * 64;
+            if (e < kP2N * GPC) {
+                int64_t n = n0 + e / GPC;
+                n = n < out ? n : out - 1;
+                sr[i] = scales[n * ng + kc * GPC + e % GPC];
+                zr[i] = zeros[n * ng + kc * GPC + e % GPC];
+            }
+        }
+    };
+    auto stash = [&](uint8_t *buf) {
+#pragma unroll
+        for (int i = 0; i < S::XCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            u32x4 v = xr[i];
+            if constexpr (kPairs) {
+                constexpr const int *P = F16Pairs<BITS>::PERM;
+                const vec a = __builtin_bit_cast(vec, v);
+                v = __builtin_bit_cast(u32x4, __builtin_shufflevector(a, a, P[0], P[1], P[2], P[3], P[4], P[5],
+                                                                      P[6], P[7]));
+            }
+            *reinterpret_cast<u32x4 *>(buf + (ch / (kP2K * 2 / 16)) * S::XROW + (ch % (kP2K * 2 / 16)) * 16) = v;
+        }
+        // a 16-byte piece holds 16 / UB units starting at an even unit: the
+        // even ones go to the group's first half, the odd ones to its second
+#pragma unroll
+        for (int i = 0; i < S::CCH; ++i) {
+            const int ch = tid + i * kQWaves * 64;
+            const int row = ch / (S::CRB / 16);
+            const int u0 = (ch % (S::CRB / 16)) * (16 / UB);       // first unit of the piece in the chunk row
+            const int gq = u0 / UPG, ug = u0 % UPG;
+            uint8_t *dst = buf + S::XB + row * S::CROW + gq * GB;
+            const u32x4 v = cr[i];
+            if constexpr (UB == 4) {
+                *reinterpret_cast<u32x2 *>(dst + (ug >> 1) * UB) = u32x2{v[0], v[2]};
+                *reinterpret_cast<u32x2 *>(dst + GB / 2 + (ug >> 1) * UB) = u32x2{v[1], v[3]};
+            } else {
+                *reinterpret_cast<u32x2 *>(dst + (ug >> 1) * UB) = u32x2{v[0], v[1]};
+                *reinterpret_cast<u32x2 *>(dst + GB / 2 + (ug >> 1) * UB) = u32x2{v[2], v[3]};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < S::SZ; ++i) {
+            const int e = tid + i * kQWaves * 64;
+            if (e < kP2N * GPC) {
+                reinterpret_cast<float *>(buf + S::XB + S::CB)[e] = sr[i];
+                (buf + S::XB + S::CB + kP2N * S::NGMAX * 4)[e] = zr[i];
+            }
+        }
+    };
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            acc[tt][i] = 0.f;
+    fetch(0);
+    stash(lds);
+    __syncthreads();
+    const int row = wave * 32 + l32;
+    for (int64_t kc = 0; kc < chunks; ++kc) {
+        const uint8_t *buf = lds + (kc & 1) * S::BUF;
+        if (kc + 1 < chunks)
+            fetch(kc + 1);
+        const float *sbuf = reinterpret_cast<const float *>(buf + S::XB + S::CB);
+        const uint8_t *zbuf = buf + S::XB + S::CB + kP2N * S::NGMAX * 4;
+#pragma unroll
+        for (int gq = 0; gq < GPC; ++gq) {
+            // this lane half's units of the group: STEPS units of UB bytes
+            uint32_t wv[STEPS * UB / 4];
+            const uint8_t *src = buf + S::XB + row * S::CROW + gq * GB + kh * (GB / 2);
+            if constexpr ((STEPS * UB) % 16 == 0) {
+#pragma unroll
+                for (int q = 0; q < STEPS * UB / 16; ++q) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 16 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wv[4 * q + e] = v[e];
+                }
+            } else {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
+                wv[0] = v[0];
+                wv[1] = v[1];
+            }
+            const float scale = sbuf[row * GPC + gq];
+            const int zero = zbuf[row * GPC + gq];
+            vec b[STEPS];
+            if constexpr (kPairs) {
+                const f16 zb = static_cast<f16>(1024 + zero);           // exact: at most 1279
+                const f16x2 z2 = {zb, zb};
+                const uint32_t mask = F16Pairs<BITS>::kMask, magic = 0x64006400u;
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st) {
+                    uint32_t u[4];
+                    F16Pairs<BITS>::make(&wv[st * UB / 4], u, mask, magic);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const f16x2 d = __builtin_bit_cast(f16x2, u[p]) - z2;   // exact
+                        b[st][2 * p] = d[0];
+                        b[st][2 * p + 1] = d[1];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 8 * st + e;                   // code j of the lane's STEPS units
+                        const int code = (int)((wv[(j * BITS) / 32] >> ((j * BITS) % 32)) & cmask);
+                        b[st][e] = static_cast<TX>(static_cast<float>(code - zero));   // exact
+                    }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                // X of token 32 tt + l32, columns 16 st + 8 kh .. + 7 of the group
+                const uint8_t *xp = buf + (tt * 32 + l32) * S::XROW + (gq * G + 8 * kh) * 2;
+                f32x16 part;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    part[i] = 0.f;
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st)
+                    part = QOp32<TX>::mfma(*reinterpret_cast<const vec *>(xp + 32 * st), b[st], part);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[tt][i] = fmaf(scale, part[i], acc[tt][i]);
+            }
+        }
+        if (kc + 1 < chunks)
+            stash(lds + ((kc + 1) & 1) * S::BUF);
+        __syncthreads();
+    }
+    // lane l, register i: token 8 (i / 4) + 4 (l / 32) + i % 4 of the tile, row l % 32
+    const int64_t nn = n0 + row;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t m = m0 + tt * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
+            if (m < M && nn < out) {
+                if (YF32)
+                    static_cast<float *>(Y)[m * out + nn] = acc[tt][i];
+                else
+                    static_cast<TX *>(Y)[m * out + nn] = static_cast<TX>(acc[tt][i]);
+            }
+        }
+}
+
 template <typename TX, int BITS, int G>
 static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t *qweight,
                            const float *scales, const uint8_t *zeros, int64_t out, void *Y, bool yf32,
@@ -591,6 +828,14 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
         if (yf32) AWQ_QGEMM(1, 2, true); else AWQ_QGEMM(1, 2, false);
     } else if (M <= 64) {
         if (yf32) AWQ_QGEMM(1, 4, true); else AWQ_QGEMM(1, 4, false);
+    } else if (in % kP2K == 0 && ((out + kP2N - 1) / kP2N) * ((M + kP2M - 1) / kP2M) >= 256) {
+        const dim3 grid((unsigned)((out + kP2N - 1) / kP2N), (unsigned)((M + kP2M - 1) / kP2M));
+        if (yf32)
+            hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, true>), grid, block, 0, st, (const TX *)X, M, in,
+                               qweight, scales, zeros, out, Y);
+        else
+            hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, false>), grid, block, 0, st, (const TX *)X, M, in,
+                               qweight, scales, zeros, out, Y);
     } else if (in % kPfK != 0 || ((out + kPfN - 1) / kPfN) * ((M + kPfM - 1) / kPfM) < 256) {
         if (yf32) AWQ_QGEMM(2, 4, true); else AWQ_QGEMM(2, 4, false);
     } else {
