@@ -594,28 +594,31 @@ template <> struct QOp32<bf16> {
     }
 };
 
-template <int BITS>
+template <int BITS, int RT>
 struct P2Stage {
+    static constexpr int N = kP2N * RT;                         // rows per block
     static constexpr int XROW = kP2K * 2 + 16;                  // LDS bytes per token row (padded)
     static constexpr int XB = kP2M * XROW;
     static constexpr int CRB = kP2K * BITS / 8;                 // code bytes of one row in a chunk
     static constexpr int CROW = CRB + 16;
-    static constexpr int CB = kP2N * CROW;
+    static constexpr int CB = N * CROW;
     static constexpr int NGMAX = kP2K / 32;
-    static constexpr int BUF = XB + CB + kP2N * NGMAX * 4 + kP2N * NGMAX;
+    static constexpr int BUF = XB + CB + N * NGMAX * 4 + N * NGMAX;
     static constexpr int XCH = kP2M * kP2K * 2 / 16 / (kQWaves * 64);   // 16-byte X chunks per thread (2)
-    static constexpr int CCH = kP2N * CRB / 16 / (kQWaves * 64);        // 16-byte code chunks per thread
-    static constexpr int SZ = (kP2N * NGMAX + kQWaves * 64 - 1) / (kQWaves * 64);   // scales per thread
+    static constexpr int CCH = N * CRB / 16 / (kQWaves * 64);           // 16-byte code chunks per thread
+    static constexpr int SZ = (N * NGMAX + kQWaves * 64 - 1) / (kQWaves * 64);   // scales per thread
 };
 
-template <typename TX, int BITS, int G, bool YF32>
+// RT: 32-row tiles per wave (the block has 256 RT rows); with RT = 2 each
+// X fragment read from LDS serves 64 rows.
+template <typename TX, int BITS, int G, bool YF32, int RT>
 __global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf32(const TX *__restrict__ X, int64_t M, int64_t in,
                                                              const uint32_t *__restrict__ qweight,
                                                              const float *__restrict__ scales,
                                                              const uint8_t *__restrict__ zeros, int64_t out,
                                                              void *__restrict__ Y)
 {
-    typedef P2Stage<BITS> S;
+    typedef P2Stage<BITS, RT> S;
     typedef typename QOp<TX>::vec vec;
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     constexpr int GPC = kP2K / G;               // groups per chunk
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf32(const TX *__restric
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, kh = lane >> 5;
-    const int64_t m0 = (int64_t)blockIdx.y * kP2M, n0 = (int64_t)blockIdx.x * kP2N;
+    const int64_t m0 = (int64_t)blockIdx.y * kP2M, n0 = (int64_t)blockIdx.x * S::N;
     const int64_t ng = in / G, row_bytes = in * BITS / 8;
     const int64_t chunks = in / kP2K;
     const uint8_t *qbytes = reinterpret_cast<const uint8_t *>(qweight);
@@ -655,7 +658,7 @@ __global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf32(const TX *__restric
 #pragma unroll
         for (int i = 0; i < S::SZ; ++i) {
             const int e = tid + i * kQWaves * 64;
-            if (e < kP2N * GPC) {
+            if (e < S::N * GPC) {
                 int64_t n = n0 + e / GPC;
                 n = n < out ? n : out - 1;
                 sr[i] = scales[n * ng + kc * GPC + e % GPC];
@@ -697,89 +700,103 @@ __global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf32(const TX *__restric
 #pragma unroll
         for (int i = 0; i < S::SZ; ++i) {
             const int e = tid + i * kQWaves * 64;
-            if (e < kP2N * GPC) {
+            if (e < S::N * GPC) {
                 reinterpret_cast<float *>(buf + S::XB + S::CB)[e] = sr[i];
-                (buf + S::XB + S::CB + kP2N * S::NGMAX * 4)[e] = zr[i];
+                (buf + S::XB + S::CB + S::N * S::NGMAX * 4)[e] = zr[i];
             }
         }
     };
 
-    f32x16 acc[2];
+    f32x16 acc[RT][2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            acc[tt][i] = 0.f;
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                acc[rt][tt][i] = 0.f;
     fetch(0);
     stash(lds);
     __syncthreads();
-    const int row = wave * 32 + l32;
     for (int64_t kc = 0; kc < chunks; ++kc) {
         const uint8_t *buf = lds + (kc & 1) * S::BUF;
         if (kc + 1 < chunks)
             fetch(kc + 1);
         const float *sbuf = reinterpret_cast<const float *>(buf + S::XB + S::CB);
-        const uint8_t *zbuf = buf + S::XB + S::CB + kP2N * S::NGMAX * 4;
+        const uint8_t *zbuf = buf + S::XB + S::CB + S::N * S::NGMAX * 4;
 #pragma unroll
         for (int gq = 0; gq < GPC; ++gq) {
-            // this lane half's units of the group: STEPS units of UB bytes
-            uint32_t wv[STEPS * UB / 4];
-            const uint8_t *src = buf + S::XB + row * S::CROW + gq * GB + kh * (GB / 2);
-            if constexpr ((STEPS * UB) % 16 == 0) {
+            vec b[RT][STEPS];
+            float scale[RT];
 #pragma unroll
-                for (int q = 0; q < STEPS * UB / 16; ++q) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 16 * q);
+            for (int rt = 0; rt < RT; ++rt) {
+                const int row = (wave * RT + rt) * 32 + l32;
+                // this lane half's units of the group: STEPS units of UB bytes
+                uint32_t wv[STEPS * UB / 4];
+                const uint8_t *src = buf + S::XB + row * S::CROW + gq * GB + kh * (GB / 2);
+                if constexpr ((STEPS * UB) % 16 == 0) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        wv[4 * q + e] = v[e];
-                }
-            } else {
-                const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
-                wv[0] = v[0];
-                wv[1] = v[1];
-            }
-            const float scale = sbuf[row * GPC + gq];
-            const int zero = zbuf[row * GPC + gq];
-            vec b[STEPS];
-            if constexpr (kPairs) {
-                const f16 zb = static_cast<f16>(1024 + zero);           // exact: at most 1279
-                const f16x2 z2 = {zb, zb};
-                const uint32_t mask = F16Pairs<BITS>::kMask, magic = 0x64006400u;
+                    for (int q = 0; q < STEPS * UB / 16; ++q) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 16 * q);
 #pragma unroll
-                for (int st = 0; st < STEPS; ++st) {
-                    uint32_t u[4];
-                    F16Pairs<BITS>::make(&wv[st * UB / 4], u, mask, magic);
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const f16x2 d = __builtin_bit_cast(f16x2, u[p]) - z2;   // exact
-                        b[st][2 * p] = d[0];
-                        b[st][2 * p + 1] = d[1];
+                        for (int e = 0; e < 4; ++e)
+                            wv[4 * q + e] = v[e];
                     }
+                } else {
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
+                    wv[0] = v[0];
+                    wv[1] = v[1];
                 }
-            } else {
+                scale[rt] = sbuf[row * GPC + gq];
+                const int zero = zbuf[row * GPC + gq];
+                if constexpr (kPairs) {
+                    const f16 zb = static_cast<f16>(1024 + zero);           // exact: at most 1279
+                    const f16x2 z2 = {zb, zb};
+                    const uint32_t mask = F16Pairs<BITS>::kMask, magic = 0x64006400u;
 #pragma unroll
-                for (int st = 0; st < STEPS; ++st)
+                    for (int st = 0; st < STEPS; ++st) {
+                        uint32_t u[4];
+                        F16Pairs<BITS>::make(&wv[st * UB / 4], u, mask, magic);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = 8 * st + e;                   // code j of the lane's STEPS units
-                        const int code = (int)((wv[(j * BITS) / 32] >> ((j * BITS) % 32)) & cmask);
-                        b[st][e] = static_cast<TX>(static_cast<float>(code - zero));   // exact
+                        for (int p = 0; p < 4; ++p) {
+                            const f16x2 d = __builtin_bit_cast(f16x2, u[p]) - z2;   // exact
+                            b[rt][st][2 * p] = d[0];
+                            b[rt][st][2 * p + 1] = d[1];
+                        }
                     }
+                } else {
+#pragma unroll
+                    for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int j = 8 * st + e;               // code j of the lane's STEPS units
+                            const int code = (int)((wv[(j * BITS) / 32] >> ((j * BITS) % 32)) & cmask);
+                            b[rt][st][e] = static_cast<TX>(static_cast<float>(code - zero));   // exact
+                        }
+                }
             }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                // X of token 32 tt + l32, columns 16 st + 8 kh .. + 7 of the group
+                // X of token 32 tt + l32, columns 16 st + 8 kh .. + 7 of the group: one read for RT row tiles
                 const uint8_t *xp = buf + (tt * 32 + l32) * S::XROW + (gq * G + 8 * kh) * 2;
-                f32x16 part;
+                f32x16 part[RT];
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    part[i] = 0.f;
+                for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int st = 0; st < STEPS; ++st)
-                    part = QOp32<TX>::mfma(*reinterpret_cast<const vec *>(xp + 32 * st), b[st], part);
+                    for (int i = 0; i < 16; ++i)
+                        part[rt][i] = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    acc[tt][i] = fmaf(scale, part[i], acc[tt][i]);
+                for (int st = 0; st < STEPS; ++st) {
+                    const vec xa = *reinterpret_cast<const vec *>(xp + 32 * st);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        part[rt] = QOp32<TX>::mfma(xa, b[rt][st], part[rt]);
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        acc[rt][tt][i] = fmaf(scale[rt], part[rt][i], acc[rt][tt][i]);
             }
         }
         if (kc + 1 < chunks)
@@ -787,19 +804,22 @@ __global__ __launch_bounds__(kQWaves * 64) void k_qgemm_pf32(const TX *__restric
         __syncthreads();
     }
     // lane l, register i: token 8 (i / 4) + 4 (l / 32) + i % 4 of the tile, row l % 32
-    const int64_t nn = n0 + row;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int rt = 0; rt < RT; ++rt) {
+        const int64_t nn = n0 + (wave * RT + rt) * 32 + l32;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t m = m0 + tt * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
-            if (m < M && nn < out) {
-                if (YF32)
-                    static_cast<float *>(Y)[m * out + nn] = acc[tt][i];
-                else
-                    static_cast<TX *>(Y)[m * out + nn] = static_cast<TX>(acc[tt][i]);
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int64_t m = m0 + tt * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
+                if (m < M && nn < out) {
+                    if (YF32)
+                        static_cast<float *>(Y)[m * out + nn] = acc[rt][tt][i];
+                    else
+                        static_cast<TX *>(Y)[m * out + nn] = static_cast<TX>(acc[rt][tt][i]);
+                }
             }
-        }
+    }
 }
 
 template <typename TX, int BITS, int G>
@@ -808,6 +828,10 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
                            hipStream_t st)
 {
     const dim3 block(kQWaves * 64);
+    // two 32-row tiles per wave in the 32 x 32 prefill tile: 4-bit codes in
+    // groups of 128 only (other widths and groups exceed the LDS or spill)
+    constexpr bool kPf32x2 = BITS == 4 && G == 128;
+    const bool pf32x2 = kPf32x2;
     // decode (M <= 16): 16 tokens and 16 rows per block, or 32 rows on layers
     // with at least 8192 rows (twice the bytes staged per round; enough blocks
     // remain to fill the chip); the 64-token x 128-row prefill tile when it
@@ -828,13 +852,23 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
         if (yf32) AWQ_QGEMM(1, 2, true); else AWQ_QGEMM(1, 2, false);
     } else if (M <= 64) {
         if (yf32) AWQ_QGEMM(1, 4, true); else AWQ_QGEMM(1, 4, false);
+    } else if (pf32x2 && in % kP2K == 0 && ((out + 2 * kP2N - 1) / (2 * kP2N)) * ((M + kP2M - 1) / kP2M) >= 256) {
+        if constexpr (kPf32x2) {
+            const dim3 grid((unsigned)((out + 2 * kP2N - 1) / (2 * kP2N)), (unsigned)((M + kP2M - 1) / kP2M));
+            if (yf32)
+                hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, true, 2>), grid, block, 0, st, (const TX *)X, M, in,
+                                   qweight, scales, zeros, out, Y);
+            else
+                hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, false, 2>), grid, block, 0, st, (const TX *)X, M,
+                                   in, qweight, scales, zeros, out, Y);
+        }
     } else if (in % kP2K == 0 && ((out + kP2N - 1) / kP2N) * ((M + kP2M - 1) / kP2M) >= 256) {
         const dim3 grid((unsigned)((out + kP2N - 1) / kP2N), (unsigned)((M + kP2M - 1) / kP2M));
         if (yf32)
-            hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, true>), grid, block, 0, st, (const TX *)X, M, in,
+            hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, true, 1>), grid, block, 0, st, (const TX *)X, M, in,
                                qweight, scales, zeros, out, Y);
         else
-            hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, false>), grid, block, 0, st, (const TX *)X, M, in,
+            hipLaunchKernelGGL((k_qgemm_pf32<TX, BITS, G, false, 1>), grid, block, 0, st, (const TX *)X, M, in,
                                qweight, scales, zeros, out, Y);
     } else if (in % kPfK != 0 || ((out + kPfN - 1) / kPfN) * ((M + kPfM - 1) / kPfM) < 256) {
         if (yf32) AWQ_QGEMM(2, 4, true); else AWQ_QGEMM(2, 4, false);

@@ -104,6 +104,10 @@ CASES = [
     # the 64-token x 128-row prefill tile (at least 256 blocks, in a multiple of 128)
     ("bf16", 4, 128, "sym", 1000, 4000, 256),    # ragged token and row tiles
     ("f16", 8, 64, "asym", 1100, 3900, 128),
+    # the 32 x 32 prefill tile with two 32-row tiles per wave (4-bit, group 128,
+    # 512-row blocks): ragged token and row tiles in both input types
+    ("bf16", 4, 128, "asym", 2100, 4100, 256),
+    ("f16", 4, 128, "sym", 2050, 4097, 128),
     ("f16", 4, 32, "sym", 2048, 2048, 128),
     # more than 32 tokens, fewer blocks or in not a multiple of 128: the 32-token tile
     ("bf16", 4, 128, "sym", 200, 130, 1024),
