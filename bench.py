@@ -362,7 +362,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the AWQ search of one layer is measured on a "
-              "single MI355X (sharding over GPUs is described in DESIGN.md, not run).",
+              "single MI355X; several GPUs would each search their own rows of the layer "
+              "(the row blocks are independent), which this measurement does not run.",
               file=sys.stderr)
         sys.exit(2)
 
