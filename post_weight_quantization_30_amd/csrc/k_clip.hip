@@ -95,8 +95,16 @@ template <> struct ClipMma<f16> {
             // both the stored part and the difference use.
             const f32x2 x = {opaque(d[e]), opaque(d[e + 1])};
             const f16x2 h = __builtin_convertvector(x, f16x2);
-            const f32x2 hf = __builtin_convertvector(h, f32x2);
-            const f16x2 l = __builtin_convertvector(f32x2{x[0] - hf[0], x[1] - hf[1]}, f16x2);  // exact differences
+            // x - f32(hi) in one v_fma_mix_f32 each (the fp16 half widened
+            // exactly, times -1, plus x, rounded once): the difference is
+            // exact in fp32, so this is the same value as widen-then-subtract
+            const uint32_t hp = __builtin_bit_cast(uint32_t, h);
+            const float m1 = -1.0f;
+            float l0, l1;
+            asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(l0) : "v"(hp), "v"(m1), "v"(x[0]));
+            asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(l1)
+                : "v"(hp), "v"(m1), "v"(x[1]));
+            const f16x2 l = __builtin_convertvector(f32x2{l0, l1}, f16x2);
             p[0][e] = h[0];
             p[0][e + 1] = h[1];
             p[1][e] = l[0];
