@@ -78,7 +78,13 @@ __device__ __forceinline__ void potrf64(double *A, int64_t n, int64_t k0)
             // 1/sqrt of the pivot once, then products (no fp64 divide on the
             // step's serial path)
             const double p = bcast(a[j >> 2], j);
-            const double rs = rsqrt(p);
+            // 1/sqrt(p): the hardware estimate and one Newton step (three
+            // dependent operations on the step's serial path instead of the
+            // library's refinement chain); the step roughly doubles the
+            // estimate's correct bits, past fp64 precision
+            const double y0 = __builtin_amdgcn_rsq(p);
+            const double e = fma(-(p * y0), y0, 1.0);
+            const double rs = fma(0.5 * y0, e, y0);
             double v = a[j >> 2];
             v = i == j ? p * rs : (i > j ? v * rs : v);
             a[j >> 2] = v;
