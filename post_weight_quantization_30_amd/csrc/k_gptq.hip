@@ -94,8 +94,8 @@ __device__ __forceinline__ void potrf64(double *A, int64_t n, int64_t k0)
         const double lij = cb[i];
 #pragma unroll
         for (int t = 0; t < kNb / 4; ++t)
-            if (4 * t + w > j)                     // uniform per wave
-                a[t] -= lij * cb[4 * t + w];
+            if (4 * t + w > j)                     // uniform per wave; one rounding
+                a[t] = fma(-lij, cb[4 * t + w], a[t]);
     }
 #pragma unroll
     for (int t = 0; t < kNb / 4; ++t)
