@@ -834,11 +834,13 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
     const bool pf32x2 = kPf32x2;
     // decode (M <= 16): 16 tokens and 16 rows per block, or 32 rows on layers
     // with at least 8192 rows (twice the bytes staged per round; enough blocks
-    // remain to fill the chip); the 64-token x 128-row prefill tile when it
-    // gives at least one block per compute unit (and in is a multiple of 128);
-    // otherwise split over K inside the block, 16 tokens x 32 rows up to 32
-    // tokens, 16 x 64 up to 64 and 32 x 64 beyond (measured: the smaller tiles
-    // win while their extra blocks still fit the chip at once).
+    // remain to fill the chip). Beyond 64 tokens, with in a multiple of 128,
+    // the first prefill tile that gives at least one block per compute unit:
+    // 32 x 32 MFMAs with 64 tokens x 512 rows (4-bit codes in groups of 128),
+    // then 64 x 256, then the 16 x 16 tile with 64 x 128. Otherwise split
+    // over K inside the block, 16 tokens x 32 rows up to 32 tokens, 16 x 64
+    // up to 64 and 32 x 64 beyond (measured: the smaller tiles win while
+    // their extra blocks still fit the chip at once).
 #define AWQ_QGEMM(MT, NT, YF)                                                                        \
     hipLaunchKernelGGL((k_qgemm<TX, BITS, G, MT, NT, YF>),                                            \
                        dim3((unsigned)((out + 16 * NT - 1) / (16 * NT)),                             \
