@@ -108,6 +108,8 @@ CASES = [
     # 512-row blocks): ragged token and row tiles in both input types
     ("bf16", 4, 128, "asym", 2100, 4100, 256),
     ("f16", 4, 128, "sym", 2050, 4097, 128),
+    # one 32-row tile per wave (groups of 64), three K chunks, ragged edges
+    ("bf16", 4, 64, "sym", 1030, 4100, 384),
     ("f16", 4, 32, "sym", 2048, 2048, 128),
     # more than 32 tokens, fewer blocks or in not a multiple of 128: the 32-token tile
     ("bf16", 4, 128, "sym", 200, 130, 1024),
