@@ -17,9 +17,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libawq.so")
 SOURCES = ["abi.hip", "k_stats.hip", "k_search.hip", "k_pack.hip", "k_clip.hip", "k_fold.hip", "k_qgemm.hip", "k_gptq.hip"]
-# Standalone measurement program: the attainable MFMA peak (bench.py runs it).
-PROBE_SRC = "mfma_peak.hip"
-PROBE = os.path.join(PKG, "mfma_peak")
+# k_search16.hip is compiled once per (operand type, group size), in parallel:
+# (source, extra flags, object name).
+VARIANTS = [("k_search16.hip", [f"-DAWQ_S16_T={t}", f"-DAWQ_S16_G={g}"], f"k_search16_{t}_g{g}.o")
+            for t in ("f16", "bf16") for g in (32, 64, 128)]
+# Standalone measurement programs: the attainable MFMA peak (bench.py runs
+# it) and the microbenchmarks behind the kernel design (mb_gfx950).
+PROBES = [("mfma_peak.hip", os.path.join(PKG, "mfma_peak")),
+          ("mb_gfx950.hip", os.path.join(PKG, "mb_gfx950"))]
 ARCH = "gfx950"
 
 CFLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-ffp-contract=off",
@@ -34,9 +39,10 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job, verbose):
+    src, extra, objname = job if isinstance(job, tuple) else (job, [], os.path.splitext(job)[0] + ".o")
+    obj = os.path.join(BUILD, objname)
+    cmd = [_hipcc(), *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,8 +55,9 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    jobs = VARIANTS + SOURCES   # the slowest first
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 8)) as ex:
+        results = list(ex.map(lambda s: _compile(s, verbose), jobs))
     for _, out in results:
         if out and verbose:
             print(out)
@@ -60,13 +67,14 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
-    cmd = [_hipcc(), *[f for f in CFLAGS if f != "-fPIC"], os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}{r.stderr}")
-    os.replace(PROBE + ".tmp", PROBE)
+    for src, exe in PROBES:
+        cmd = [_hipcc(), *[f for f in CFLAGS if f != "-fPIC"], os.path.join(CSRC, src), "-o", exe + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+        os.replace(exe + ".tmp", exe)
     return LIB
 
 

@@ -149,7 +149,7 @@ int awq_search_candidates(const void *W, const void *X, int dtype, int64_t out, 
                                          (const float *)(base + lay.inv_off),
                                          (const int32_t *)(base + lay.unit_off), grid + 1, bits,
                                          group, mode, (double *)(base + lay.part_off),
-                                         (hipStream_t)stream));
+                                         base + lay.xf_off, (hipStream_t)stream));
 }
 
 int awq_search_finish(int64_t out, int64_t in, int64_t tokens, int grid, double *mse,

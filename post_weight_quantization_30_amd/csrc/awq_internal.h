@@ -56,7 +56,7 @@ __device__ __forceinline__ float opaque(float x)
 
 // Workspace layout of awq_search (each part 256-byte aligned).
 struct SearchWs {
-    size_t s_off, inv_off, unit_off, part_off, total;
+    size_t s_off, inv_off, unit_off, part_off, xf_off, total;
     int64_t nblk;
 };
 
@@ -77,7 +77,11 @@ inline SearchWs search_ws_layout(int64_t out, int64_t in, int64_t tokens, int gr
     w.inv_off = align256((size_t)(na * in) * sizeof(float));
     w.unit_off = w.inv_off + align256((size_t)(na * in) * sizeof(float));
     w.part_off = w.unit_off + align256((size_t)na * sizeof(int32_t));
-    w.total = w.part_off + align256((size_t)(na * w.nblk) * sizeof(double));
+    // X of a 16-bit layer rearranged into matrix-operand fragment order (see
+    // k_search16.hip), zero-padded to whole 256-token blocks.
+    w.xf_off = w.part_off + align256((size_t)(na * w.nblk) * sizeof(double));
+    const int64_t tpad = ((tokens + kTokPerBlock - 1) / kTokPerBlock) * kTokPerBlock;
+    w.total = w.xf_off + align256((size_t)(tpad * in) * 2);
     return w;
 }
 
@@ -89,8 +93,27 @@ hipError_t launch_s_table(const float *xmag, int64_t in, int grid, float *s_tab,
 hipError_t launch_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                          int64_t tokens, const float *s_tab, const float *inv_tab,
                          const int32_t *unit, int n_alpha, int bits, int group, int mode,
-                         double *partial, hipStream_t st);
+                         double *partial, void *xfrag, hipStream_t st);
 bool search_uses_fp32_operands(int dtype, int64_t out, int64_t tokens);
+// The 32x32-tile search for 16-bit operands (k_search16.hip): whether it
+// takes this shape, and its launcher (same contract as launch_search),
+// which dispatches to one launcher per operand type and group size.
+bool search16_applies(int64_t in, int n_alpha, int64_t nblocks);
+hipError_t launch_search16(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                           int64_t tokens, const float *s_tab, const float *inv_tab,
+                           const int32_t *unit, int n_alpha, int bits, int group, int mode,
+                           double *partial, void *xfrag, hipStream_t st);
+#define AWQ_S16_DECL(name)                                                                          \
+    hipError_t name(const void *W, const void *X, int64_t out, int64_t in, int64_t tokens,          \
+                    const float *s_tab, const float *inv_tab, const int32_t *unit, int n_alpha,     \
+                    int bits, int mode, double *partial, void *xfrag, hipStream_t st);
+AWQ_S16_DECL(launch_search16_f16_g32)
+AWQ_S16_DECL(launch_search16_f16_g64)
+AWQ_S16_DECL(launch_search16_f16_g128)
+AWQ_S16_DECL(launch_search16_bf16_g32)
+AWQ_S16_DECL(launch_search16_bf16_g64)
+AWQ_S16_DECL(launch_search16_bf16_g128)
+#undef AWQ_S16_DECL
 hipError_t launch_reduce_argmin(const double *partial, int64_t nblk, int n_alpha, int64_t out,
                                 int64_t tokens, int64_t in, const float *s_tab, double *mse,
                                 int32_t *best, float *s_best, hipStream_t st);

@@ -706,12 +706,39 @@ bool search_uses_fp32_operands(int dtype, int64_t out, int64_t tokens)
     return dtype == AWQ_F32 || out < kMinRows16 || tokens < kMinTokens16;
 }
 
+// The 32x32 search (k_search16.hip) takes 16-bit operands with `in` a
+// multiple of 128 and passes of 9..12 candidates (n_alpha >= 9).
+bool search16_applies(int64_t in, int n_alpha, int64_t nblocks)
+{
+    const int npass = (n_alpha + 11) / 12;
+    return in % 128 == 0 && n_alpha / npass >= 9 && nblocks * npass <= 0x7fffffffLL;
+}
+
+hipError_t launch_search16(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                           int64_t tokens, const float *s_tab, const float *inv_tab,
+                           const int32_t *unit, int n_alpha, int bits, int group, int mode,
+                           double *partial, void *xfrag, hipStream_t st)
+{
+#define AWQ_S16_CALL(name) name(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, mode, partial, xfrag, st)
+    if (dtype == AWQ_F16)
+        return group == 32 ? AWQ_S16_CALL(launch_search16_f16_g32)
+             : group == 64 ? AWQ_S16_CALL(launch_search16_f16_g64)
+                           : AWQ_S16_CALL(launch_search16_f16_g128);
+    return group == 32 ? AWQ_S16_CALL(launch_search16_bf16_g32)
+         : group == 64 ? AWQ_S16_CALL(launch_search16_bf16_g64)
+                       : AWQ_S16_CALL(launch_search16_bf16_g128);
+#undef AWQ_S16_CALL
+}
+
 hipError_t launch_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                          int64_t tokens, const float *s_tab, const float *inv_tab,
                          const int32_t *unit, int n_alpha, int bits, int group, int mode,
-                         double *partial, hipStream_t st)
+                         double *partial, void *xfrag, hipStream_t st)
 {
     const bool wide = search_uses_fp32_operands(dtype, out, tokens);
+    if (!wide && search16_applies(in, n_alpha, ((out + 15) / 16) * ((tokens + kTokPerBlock - 1) / kTokPerBlock)))
+        return launch_search16(W, X, dtype, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group,
+                               mode, partial, xfrag, st);
     switch (dtype) {
     case AWQ_F32:
         return search_group<float, float>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st);
