@@ -90,7 +90,10 @@ int awq_s_table(const float *xmag, int64_t in, int grid, float *s_table, void *s
  *   s_best:  device fp32[in] (output): s_table[best], or all ones when best = -1.
  *            Deploy by multiplying W's columns by it and dividing the layer's
  *            input by it upstream.
- *   ws:      device scratch of at least awq_search_workspace_size(...) bytes.
+ *   ws:      device scratch of at least awq_search_workspace_size(...) bytes:
+ *            the s-table and its reciprocals, one fp64 partial per (candidate,
+ *            block), and a 16-bit copy of X in matrix-fragment order padded to
+ *            whole 256-token blocks (used by the 16-bit path).
  * The GPU kernels evaluate the error as X (Wq - W)^T (equal to the difference
  * of the two products by linearity), accumulating in fp32 and summing squares
  * in fp64; mse is accurate to about 1e-5 relative, not bitwise. Operands are

@@ -56,8 +56,11 @@ def test_workspace_sizes(L):
     assert awq.act_stats_workspace_size(0, 10) == 0
     n = awq.search_workspace_size(4096, 4096, 256, 20)
     # s-table and its reciprocals (21 x 4096 fp32 each) + one fp64 per (candidate, block)
-    assert n >= 2 * 21 * 4096 * 4 + 21 * 256 * 8
-    assert n < 2 * 21 * 4096 * 4 + 21 * 256 * 8 + 3 * 256
+    # + a 16-bit copy of X (256 tokens x 4096) in matrix-fragment order
+    need = 2 * 21 * 4096 * 4 + 21 * 256 * 8 + 256 * 4096 * 2
+    assert need <= n < need + 4 * 256
+    # the X copy is padded to whole 256-token blocks
+    assert awq.search_workspace_size(4096, 4096, 300, 20) - n >= 256 * 4096 * 2
     assert awq.search_workspace_size(4096, 4096, 256, 0) == 0
     assert awq.search_workspace_size(4096, 4096, 256, awq.MAX_GRID + 1) == 0
 
