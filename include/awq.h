@@ -108,6 +108,26 @@ int awq_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                void *stream);
 size_t awq_search_workspace_size(int64_t out, int64_t in, int64_t tokens, int grid);
 
+/* awq_search without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation). Arguments, outputs and results are those of
+ * awq_search; the scratch is a fixed static device array of
+ * AWQ_SEARCH_NOALLOC_MAX_BYTES per GPU, held until the process ends.
+ *   - The scratch of the current device (hipGetDevice) is used: `stream` must
+ *     belong to that device. The first call on a device looks its address up
+ *     (no allocation); make that first call outside stream capture.
+ *   - AWQ_ERR_WORKSPACE when awq_search_workspace_size(out, in, tokens, grid)
+ *     exceeds AWQ_SEARCH_NOALLOC_MAX_BYTES (24 MiB: e.g. 4096 x 4096 with up to
+ *     2048 tokens, 12288 x 4096 with 2048 tokens); nothing is launched then.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *     time on one GPU (two streams, two host threads) race and must be
+ *     serialised by the caller. Nothing in the scratch has to start at zero:
+ *     each call writes every scratch byte it later reads. */
+#define AWQ_SEARCH_NOALLOC_MAX_BYTES ((size_t)24 << 20)
+int awq_search_noalloc(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                       int64_t tokens, const float *xmag, int bits, int group, int grid, int mode,
+                       double *mse, int32_t *best, float *s_best, void *stream);
+
 /* awq_search in its three stages, in this order on one stream with one
  * workspace (awq_search is exactly the three calls). They let a caller time or
  * profile the error kernel alone, and they are where a search sharded over

@@ -16,6 +16,7 @@ F32, F16, BF16 = 0, 1, 2
 SYM, ASYM = 0, 1
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP, ERR_NONFINITE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 MAX_GRID = 1024
+SEARCH_NOALLOC_MAX_BYTES = 24 << 20   # static per-GPU scratch of awq_search_noalloc
 MAX_CLIP = 64
 
 _DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
@@ -50,6 +51,9 @@ def lib():
         L.awq_search.argtypes = [vp, vp, cint, i64, i64, i64, vp, cint, cint, cint, cint,
                                  vp, vp, vp, vp, sz, vp]
         L.awq_search.restype = cint
+        L.awq_search_noalloc.argtypes = [vp, vp, cint, i64, i64, i64, vp, cint, cint, cint, cint,
+                                         vp, vp, vp, vp]
+        L.awq_search_noalloc.restype = cint
         L.awq_search_prepare.argtypes = [vp, i64, i64, i64, cint, vp, sz, vp]
         L.awq_search_prepare.restype = cint
         L.awq_search_candidates.argtypes = [vp, vp, cint, i64, i64, i64, cint, cint, cint, cint,
@@ -180,6 +184,21 @@ def search(W, X, xmag, bits, group, grid, mode, mse=None, best=None, s_best=None
         bits, group, grid, _MODE[mode], _dev(mse, "mse", torch.float64),
         _dev(best, "best", torch.int32), _dev(s_best, "s_best", torch.float32),
         _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()))
+    return mse, best, s_best
+
+
+def search_noalloc(W, X, xmag, bits, group, grid, mode, mse, best, s_best):
+    """awq_search on the library's static per-GPU scratch: the C call allocates
+    nothing. The outputs (mse fp64[grid+1], best int32[1], s_best fp32[in])
+    are the caller's. Calls that overlap on one GPU race on the scratch."""
+    out, n_in = W.shape
+    T = X.shape[0]
+    if X.shape[1] != n_in or X.dtype != W.dtype:
+        raise ValueError("W (out, in) and X (tokens, in) must share in and dtype")
+    _check("awq_search_noalloc", lib().awq_search_noalloc(
+        _dev(W, "W"), _dev(X, "X"), _dtype_code(W), out, n_in, T, _dev(xmag, "xmag", torch.float32),
+        bits, group, grid, _MODE[mode], _dev(mse, "mse", torch.float64),
+        _dev(best, "best", torch.int32), _dev(s_best, "s_best", torch.float32), _stream()))
     return mse, best, s_best
 
 

@@ -3,7 +3,9 @@
 // Every entry point validates all arguments on the host before it enqueues
 // anything; on a failed check it returns a negative status and writes nothing.
 // The library allocates no device memory: scratch comes from the caller's
-// workspace.
+// workspace, or for awq_search_noalloc from a static device array.
+#include <mutex>
+
 #include "awq_internal.h"
 
 namespace {
@@ -194,6 +196,63 @@ int awq_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
     if (st == AWQ_OK)
         st = awq_search_finish(out, in, tokens, grid, mse, best, s_best, ws, ws_bytes, stream);
     return st;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of awq_search_noalloc. Every GPU the library runs on holds its own
+// copy until the process ends. In host code `scratch` only names the symbol:
+// its device address, different on each GPU, comes from hipGetSymbolAddress
+// with that GPU current, and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[AWQ_SEARCH_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch, looked up once per device.
+int current_scratch(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return AWQ_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return AWQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return AWQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int awq_search_noalloc(const void *W, const void *X, int dtype, int64_t out, int64_t in,
+                       int64_t tokens, const float *xmag, int bits, int group, int grid, int mode,
+                       double *mse, int32_t *best, float *s_best, void *stream)
+{
+    // Shape and size checks first: a refused call touches no device.
+    int st = check_search_shape(out, in, tokens, grid);
+    if (st != AWQ_OK)
+        return st;
+    if (awq::search_ws_layout(out, in, tokens, grid).total > AWQ_SEARCH_NOALLOC_MAX_BYTES)
+        return AWQ_ERR_WORKSPACE;
+    if (!W || !X || !xmag || !mse || !best || !s_best)
+        return AWQ_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    st = current_scratch(&ws);
+    if (st != AWQ_OK)
+        return st;
+    return awq_search(W, X, dtype, out, in, tokens, xmag, bits, group, grid, mode, mse, best,
+                      s_best, ws, AWQ_SEARCH_NOALLOC_MAX_BYTES, stream);
 }
 
 int awq_quantize_pack(const void *W, int dtype, int64_t out, int64_t in, const float *s, int bits,
