@@ -88,7 +88,8 @@ def measured_mfma_peak():
 
 def cpu_baseline(spec, lay, target_s):
     """The oracle as it stands, on the first R rows of the same layer (all tokens,
-    all columns, every candidate), R grown until the run takes ~target_s."""
+    all columns, every candidate), R grown until the run takes ~target_s.
+    Returns the timing record and the oracle's results for the R rows."""
     import numpy as np
     from oracle import oracle as ref
     from post_weight_quantization_30_amd import synth
@@ -100,16 +101,48 @@ def cpu_baseline(spec, lay, target_s):
         Wf = synth.storage_to_f32(lay["W"][:rows], spec.dtype)
         t0 = time.perf_counter()
         xmag = ref.act_stats(Xf)
-        _, best, s_best, _ = ref.search(Wf, Xf, xmag, spec.bits, spec.group, spec.grid, spec.mode)
-        ref.quantize_pack(Wf, s_best, spec.bits, spec.group, spec.mode)
+        mse, best, s_best, _ = ref.search(Wf, Xf, xmag, spec.bits, spec.group, spec.grid, spec.mode)
+        packed = ref.quantize_pack(Wf, s_best, spec.bits, spec.group, spec.mode)
         dt = time.perf_counter() - t0
         if dt >= target_s / 3 or rows >= spec.out:
             break
         rows = min(spec.out, int(rows * max(2.0, min(8.0, target_s / max(dt, 1e-3)))))
     macs = spec.n_alpha * spec.tokens * rows * spec.inn
-    return {"value": macs / dt, "unit": "alpha-candidate MAC/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {spec.out} rows, all {spec.tokens} tokens and {spec.inn} columns, "
-                      f"{spec.n_alpha} candidates; stats + search + pack; {dt:.2f} s"}
+    rec = {"value": macs / dt, "unit": "alpha-candidate MAC/s", "cores": threads, "kind": "oracle",
+           "sample": f"{rows} of {spec.out} rows, all {spec.tokens} tokens and {spec.inn} columns, "
+                     f"{spec.n_alpha} candidates; stats + search + pack; {dt:.2f} s"}
+    return rec, {"rows": rows, "xmag": xmag, "mse": np.asarray(mse), "best": int(best),
+                 "s_best": np.asarray(s_best, np.float32), "packed": packed}
+
+
+MSE_RTOL = 1e-3
+
+
+def parity_record(awq, torch, spec, W, X, xmag, full, o):
+    """The GPU's results on the oracle's rows against the oracle's: statistics
+    bitwise, every candidate error within 1e-3 relative, the same choice unless
+    the oracle's errors at the two choices lie within 1e-3 relative, and the
+    packed codes, scales and zeros bitwise for the oracle's s."""
+    import numpy as np
+    rows = o["rows"]
+    if rows == spec.out:
+        mse_g, best_g = full
+    else:
+        m, b, _ = awq.search(W[:rows].contiguous(), X, xmag, spec.bits, spec.group, spec.grid, spec.mode)
+        mse_g, best_g = m.cpu().numpy(), int(b.item())
+    mse_o, best_o = o["mse"], o["best"]
+    rel = float(np.max(np.abs(mse_g - mse_o) / np.abs(mse_o)))
+    same_choice = best_g == best_o or bool(mse_o[best_g] <= (1 + MSE_RTOL) * mse_o[best_o])
+    s_o = torch.from_numpy(np.ascontiguousarray(o["s_best"])).to(W.device)
+    q, sc, z = awq.quantize_pack(W[:rows].contiguous(), s_o, spec.bits, spec.group, spec.mode)
+    q_o, sc_o, z_o = o["packed"]
+    codes = (np.array_equal(q.cpu().numpy().view(np.uint32), q_o) and
+             np.array_equal(sc.cpu().numpy(), sc_o) and np.array_equal(z.cpu().numpy(), z_o))
+    stats = bool(np.array_equal(xmag.cpu().numpy(), o["xmag"]))
+    ok = stats and rel <= MSE_RTOL and same_choice and codes
+    return {"rows": rows, "of": spec.out, "xmag_bitwise": stats, "mse_max_rel_diff": rel,
+            "best_gpu": best_g, "best_oracle": best_o, "same_choice": same_choice,
+            "codes_scales_zeros_bitwise": codes, "pass": bool(ok)}
 
 
 N_CLIP, MAX_SHRINK = 20, 0.5
@@ -517,7 +550,8 @@ def main():
         torch.cuda.synchronize()
         rec["copy_calib_bytes"] = src.numel()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(spec, lay, args.cpu_seconds)
+        rec["cpu_baseline"], o = cpu_baseline(spec, lay, args.cpu_seconds)
+        rec["parity"] = parity_record(awq, torch, spec, W, X, xmag, (m, b), o)
     print(json.dumps(rec), flush=True)
 
 
