@@ -44,7 +44,10 @@ enum {
     AWQ_ERR_INVALID_ARG = -1, /* null pointer, size < 1, in % group != 0, bits outside [2, 8], grid < 1, bad enum */
     AWQ_ERR_WORKSPACE = -2,   /* ws_bytes below the matching *_workspace_size() (or ws == NULL with a nonzero size) */
     AWQ_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
-    AWQ_ERR_NONFINITE = -4,   /* reserved: a search whose candidate errors are all non-finite reports best = -1 on the device */
+    AWQ_ERR_NONFINITE = -4,   /* reserved, never returned by a GPU entry point: a search whose
+                               * candidate errors are all non-finite reports best = -1 in
+                               * device memory, and that flag is the only authoritative
+                               * report (the call returns before the kernels finish) */
     AWQ_ERR_UNSUPPORTED = -5  /* valid arguments outside what the GPU kernels implement (see each call) */
 };
 

@@ -430,7 +430,14 @@ int awq_ref_clip_search(const float *W, const float *X, int64_t out, int64_t in,
     if (!x64)
         return REF_EINVAL;
     int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads())
+    if (nthreads <= 0) {
+#ifdef _OPENMP
+        nthreads = omp_get_max_threads();
+#else
+        nthreads = 1;
+#endif
+    }
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
     for (int64_t o = 0; o < out; ++o) {
         float *v = (float *)malloc((size_t)group * sizeof(float));
         float *what = (float *)malloc((size_t)group * sizeof(float));

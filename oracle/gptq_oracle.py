@@ -4,34 +4,44 @@ TEST INFRASTRUCTURE ONLY: the plain, slow statement of what the GPU GPTQ path
 computes. Only the test suite, the smoke check and the benchmark's CPU
 baseline may use it; it shares no code with the HIP library.
 
-Source: "AWQ vs GPTQ Quantization Architectures Compared", section "GPTQ:
-compensate the error you just made" (the gptq_layer, group_params and rtn
-listing and the three production details after it), and "Advanced
-Quantization Algorithms: AWQ and GPTQ Explained", section 3 (the inverse
-Hessian update). In words, for W (out, in) and calibration inputs X:
+Sources: "AWQ vs GPTQ Quantization Architectures Compared", section "GPTQ:
+compensate the error you just made" (the error-compensation idea, the damped
+Hessian and the group quantizer), and "Advanced Quantization Algorithms: AWQ
+and GPTQ Explained", section 3 (the Optimal Brain Surgeon step and the
+inverse-Hessian update after each weight is fixed).
 
-  1. H = 2 X^T X over the tokens (the pages write 2 X X^T with X as
-     (in, tokens)), in fp64;
-  2. dampening: add damp * mean(diag H) to the diagonal (damp = 0.01);
-  3. U = the upper Cholesky factor of H^-1 (transpose of the lower factor);
-  4. columns in order i = 0 .. in-1, all rows at once: at the start of each
-     group fit the group parameters on the current (already corrected)
-     weights of the group's columns; round column i with them; divide its
-     rounding error by U[i, i] and subtract that times row i of U from the
-     later columns.
+The method, as this module states it. Each output row is quantised on its
+own, weight by weight in column order, against the quadratic form of the
+layer's inputs, H = 2 X^T X (X as (tokens, in)) plus damp * mean(diag H) on
+the diagonal. Once weight i of a row is fixed at its quantised value, the
+remaining free weights F = {i+1, ...} move to minimise (w' - w)^T H (w' - w)
+given the fixed ones. Optimal Brain Surgeon gives that move in terms of the
+inverse Hessian of the weights still free before the step, G = (H_FF)^-1
+over F = {i, i+1, ...}:
+
+    w_j  <-  w_j - (w_i - q_i) * G[i, j] / G[i, i]      for j > i,
+
+and the inverse Hessian of the next free set follows by eliminating index i
+from G (a rank-one update). Writing the rows of these successive inverses as
+V[i, j] = G_i[i, j] / sqrt(G_i[i, i]) (j >= i) turns the move into
+w_j -= ((w_i - q_i) / V[i, i]) * V[i, j]; V is upper triangular with
+V^T V = H^-1, which is how the GPU path factors it. The group parameters of
+a group are fitted when its first column is reached, on the weights as the
+earlier steps have moved them.
 
 Readings (the pages leave these open):
-  - the quantizer is the one the packed format stores: asymmetric (the
-    listing's group_params / rtn: range widened to contain 0, maxq = 2^b - 1,
-    zero = rne(-lo / scale)) or symmetric (L = 2^(b-1) - 1, codes q + 2^(b-1));
-    the range and the scale are computed in fp64 and the scale is rounded
-    once to fp32, the precision it is stored in, and that fp32 scale is the
-    one used for the rounding and the error (so the stored codes, scales and
-    zeros reproduce exactly the weights GPTQ compensated for); divisions in
-    fp64, ties to even (numpy's round);
+  - the quantizer is the one the packed format stores: asymmetric (range
+    widened to contain 0, maxq = 2^b - 1, zero = rne(-lo / scale)) or
+    symmetric (L = 2^(b-1) - 1, codes q + 2^(b-1)); the range and the scale
+    are computed in fp64 and the scale is rounded once to fp32, the precision
+    it is stored in, and that fp32 scale is the one used for the rounding and
+    the error (so the stored codes, scales and zeros reproduce exactly the
+    weights GPTQ compensated for); divisions in fp64, ties to even;
+  - the per-weight step evaluates (w_i - q_i) / V[i, i] once and multiplies
+    it by V[i, j], the same two roundings the GPU's column loop makes;
   - act-order (desc_act) is not part of this path: group membership would
     then follow the permuted order and the packed format has no g_idx.
-Steps 1-3 use numpy's matrix product, inverse and Cholesky as library steps.
+numpy's matrix product and inverse serve as library steps.
 """
 import numpy as np
 
@@ -43,18 +53,30 @@ def hessian(X):
 
 
 def dampen(H, damp=0.01):
-    H = H.copy()
-    H[np.diag_indices_from(H)] += damp * np.mean(np.diag(H))
-    return H
+    """H + damp * mean(diag H) * I."""
+    mean_diag = float(np.trace(H)) / H.shape[0]
+    return H + np.diag(np.full(H.shape[0], damp * mean_diag))
 
 
-def inverse_cholesky_upper(H):
-    """U with H^-1 = U^T U, U upper: the Cholesky factor of the inverse, transposed."""
-    return np.linalg.cholesky(np.linalg.inv(H)).T
+def obs_factor(H):
+    """V (in, in), upper triangular: row i is the row of weight i in the
+    inverse Hessian of the weights still free when weight i is fixed,
+    divided by the square root of its diagonal element. Computed by fixing
+    the weights one at a time and eliminating each from the inverse."""
+    n = H.shape[0]
+    G = np.linalg.inv(np.asarray(H, np.float64))
+    V = np.zeros((n, n))
+    for i in range(n):
+        pivot = G[i, i]
+        V[i, i:] = G[i, i:] / np.sqrt(pivot)
+        # weight i leaves the free set: Schur complement of its pivot
+        G[i + 1:, i + 1:] -= np.outer(G[i + 1:, i], G[i, i + 1:]) / pivot
+    return V
 
 
 def group_params(Wg, bits, mode):
-    """Scale (fp32 value) and zero for each row of the group's current weights."""
+    """Scale (an fp32 value, held in fp64) and zero of each row of a group's weights."""
+    Wg = np.asarray(Wg, np.float64)
     if mode == "asym":
         maxq = (1 << bits) - 1
         lo = np.minimum(Wg.min(axis=1), 0.0)
@@ -68,44 +90,45 @@ def group_params(Wg, bits, mode):
     return scale, np.full_like(scale, float(1 << (bits - 1)))
 
 
-def quantize_column(w, scale, zero, bits, mode):
-    """Codes (stored form) and the dequantized values of one column."""
+def round_weight(w, scale, zero, bits, mode):
+    """The stored code of one weight and the value it stands for."""
     if mode == "asym":
-        maxq = (1 << bits) - 1
-        q = np.clip(np.round(w / scale) + zero, 0, maxq)
-        return q, scale * (q - zero)
+        code = min(max(np.round(w / scale) + zero, 0.0), float((1 << bits) - 1))
+        return code, scale * (code - zero)
     L = (1 << (bits - 1)) - 1
-    q = np.clip(np.round(w / scale), -L - 1, L)
-    return q + (1 << (bits - 1)), scale * q
+    level = min(max(np.round(w / scale), float(-L - 1)), float(L))
+    return level + (1 << (bits - 1)), scale * level
 
 
 def gptq(W, X=None, bits=4, group=128, mode="asym", damp=0.01, U=None, corrected=False):
     """Returns (codes int64 (out, in), scales float32 (out, in/group),
     zeros uint8 (out, in/group), Wq fp64 (out, in) the dequantized weights)
-    and, with corrected=True, the weights each column had when it was rounded.
-    U may be passed (computed once for all rows); rows are independent given U."""
-    W = np.array(W, np.float64)
-    out, n_in = W.shape
+    and, with corrected=True, the value each weight had when it was fixed.
+    U, the factor obs_factor() returns, may be passed (it depends on X only)."""
+    W0 = np.array(W, np.float64)
+    out, n_in = W0.shape
     if n_in % group:
         raise ValueError("in must be a multiple of group")
-    if U is None:
-        U = inverse_cholesky_upper(dampen(hessian(X), damp))
+    V = obs_factor(dampen(hessian(X), damp)) if U is None else np.asarray(U, np.float64)
     codes = np.zeros((out, n_in), np.int64)
     Wq = np.zeros((out, n_in))
+    Wfix = np.zeros((out, n_in))
     scales = np.zeros((out, n_in // group), np.float32)
     zeros = np.zeros((out, n_in // group), np.uint8)
-    for i in range(n_in):
-        if i % group == 0:
-            scale, zero = group_params(W[:, i:i + group], bits, mode)
-            scales[:, i // group] = scale
-            zeros[:, i // group] = zero
-        q, wq = quantize_column(W[:, i], scale, zero, bits, mode)
-        codes[:, i] = q
-        Wq[:, i] = wq
-        err = (W[:, i] - wq) / U[i, i]
-        W[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+    for r in range(out):
+        w = W0[r].copy()                       # the row's weights as the steps move them
+        for g in range(n_in // group):
+            cols = range(g * group, (g + 1) * group)
+            sc, zr = group_params(w[None, cols.start:cols.stop], bits, mode)
+            scale, zero = float(sc[0]), float(zr[0])
+            scales[r, g], zeros[r, g] = scale, zero
+            for i in cols:
+                code, value = round_weight(w[i], scale, zero, bits, mode)
+                codes[r, i], Wq[r, i], Wfix[r, i] = code, value, w[i]
+                step = (w[i] - value) / V[i, i]
+                w[i + 1:] = w[i + 1:] - step * V[i, i + 1:]
     if corrected:
-        return codes, scales, zeros, Wq, W       # column i is no longer changed after step i
+        return codes, scales, zeros, Wq, Wfix
     return codes, scales, zeros, Wq
 
 

@@ -121,6 +121,14 @@ def _dev(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, shape):
+    """A caller-supplied tensor must have exactly this shape (checked before any
+    launch: an undersized output would be written past its end)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _dtype_code(t):
     if t.dtype not in _DTYPE:
         raise TypeError(f"unsupported dtype {t.dtype}")
@@ -152,6 +160,7 @@ def act_stats(X, xmag=None, workspace=None):
     T, n_in = X.shape
     if xmag is None:
         xmag = torch.empty(n_in, dtype=torch.float32, device=X.device)
+    _need(xmag, "xmag", (n_in,))
     ws = _workspace(act_stats_workspace_size(T, n_in), X.device, workspace)
     _check("awq_act_stats", lib().awq_act_stats(
         _dev(X, "X"), _dtype_code(X), T, n_in, _dev(xmag, "xmag", torch.float32),
@@ -163,9 +172,17 @@ def s_table(xmag, grid, out=None):
     n_in = xmag.shape[0]
     if out is None:
         out = torch.empty((grid + 1, n_in), dtype=torch.float32, device=xmag.device)
+    _need(out, "s_table", (grid + 1, n_in))
     _check("awq_s_table", lib().awq_s_table(_dev(xmag, "xmag", torch.float32), n_in, grid,
                                             _dev(out, "s_table", torch.float32), _stream()))
     return out
+
+
+def _check_search_io(n_in, grid, xmag, mse, best, s_best):
+    _need(xmag, "xmag", (n_in,))
+    _need(mse, "mse", (grid + 1,))
+    _need(best, "best", (1,))
+    _need(s_best, "s_best", (n_in,))
 
 
 def search(W, X, xmag, bits, group, grid, mode, mse=None, best=None, s_best=None, workspace=None):
@@ -178,6 +195,7 @@ def search(W, X, xmag, bits, group, grid, mode, mse=None, best=None, s_best=None
     mse = torch.empty(grid + 1, dtype=torch.float64, device=dev) if mse is None else mse
     best = torch.empty(1, dtype=torch.int32, device=dev) if best is None else best
     s_best = torch.empty(n_in, dtype=torch.float32, device=dev) if s_best is None else s_best
+    _check_search_io(n_in, grid, xmag, mse, best, s_best)
     ws = _workspace(search_workspace_size(out, n_in, T, grid), dev, workspace)
     _check("awq_search", lib().awq_search(
         _dev(W, "W"), _dev(X, "X"), _dtype_code(W), out, n_in, T, _dev(xmag, "xmag", torch.float32),
@@ -195,6 +213,7 @@ def search_noalloc(W, X, xmag, bits, group, grid, mode, mse, best, s_best):
     T = X.shape[0]
     if X.shape[1] != n_in or X.dtype != W.dtype:
         raise ValueError("W (out, in) and X (tokens, in) must share in and dtype")
+    _check_search_io(n_in, grid, xmag, mse, best, s_best)
     _check("awq_search_noalloc", lib().awq_search_noalloc(
         _dev(W, "W"), _dev(X, "X"), _dtype_code(W), out, n_in, T, _dev(xmag, "xmag", torch.float32),
         bits, group, grid, _MODE[mode], _dev(mse, "mse", torch.float64),
@@ -217,6 +236,9 @@ def search_candidates(W, X, bits, group, grid, mode, workspace):
 
 
 def search_finish(out, n_in, tokens, grid, mse, best, s_best, workspace):
+    _need(mse, "mse", (grid + 1,))
+    _need(best, "best", (1,))
+    _need(s_best, "s_best", (n_in,))
     _check("awq_search_finish", lib().awq_search_finish(
         out, n_in, tokens, grid, _dev(mse, "mse", torch.float64), _dev(best, "best", torch.int32),
         _dev(s_best, "s_best", torch.float32), _dev(workspace, "workspace"),
@@ -236,6 +258,10 @@ def clip_search(W, X, s, bits, group, mode, n_clip=20, max_shrink=0.5, clip=None
         clip = torch.empty((out, n_in // group), dtype=torch.float32, device=dev)
     if sse is None and want_sse:
         sse = torch.empty((out, n_in // group, n_clip), dtype=torch.float64, device=dev)
+    _need(s, "s", (n_in,))
+    _need(clip, "clip", (out, n_in // group))
+    if sse is not None:
+        _need(sse, "sse", (out, n_in // group, n_clip))
     _check("awq_clip_search", lib().awq_clip_search(
         _dev(W, "W"), _dev(X, "X"), _dtype_code(W), out, n_in, T, _dev(s, "s", torch.float32),
         bits, group, _MODE[mode], n_clip, float(max_shrink), _dev(clip, "clip", torch.float32),
@@ -255,6 +281,12 @@ def quantize_pack(W, s, bits, group, mode, qweight=None, scales=None, zeros=None
         scales = torch.empty((out, n_in // group), dtype=torch.float32, device=dev)
     if zeros is None:
         zeros = torch.empty((out, n_in // group), dtype=torch.uint8, device=dev)
+    _need(s, "s", (n_in,))
+    _need(qweight, "qweight", (out, words_per_row(n_in, bits)))
+    _need(scales, "scales", (out, n_in // group))
+    _need(zeros, "zeros", (out, n_in // group))
+    if clip is not None:
+        _need(clip, "clip", (out, n_in // group))
     if clip is None:
         _check("awq_quantize_pack", lib().awq_quantize_pack(
             _dev(W, "W"), _dtype_code(W), out, n_in, _dev(s, "s", torch.float32), bits, group,
@@ -319,6 +351,7 @@ def qgemm(X, qweight, scales, zeros, bits, group, y=None, y_f32=False):
         raise ValueError("qweight has the wrong number of words per row")
     ydt = torch.float32 if y_f32 else X.dtype
     y = torch.empty((M, out), dtype=ydt, device=X.device) if y is None else y
+    _need(y, "y", (M, out))
     _check("awq_qgemm", lib().awq_qgemm(
         _dev(X, "X"), _dtype_code(X), M, n_in, _dev(qweight, "qweight"),
         _dev(scales, "scales", torch.float32), _dev(zeros, "zeros", torch.uint8), out, bits, group,
@@ -336,6 +369,7 @@ def gptq_hessian(X, damp=0.01, H=None):
     """H (in, in) fp64 = 2 X^T X plus damp * mean(diag) on the diagonal."""
     T, n_in = X.shape
     H = torch.empty((n_in, n_in), dtype=torch.float64, device=X.device) if H is None else H
+    _need(H, "H", (n_in, n_in))
     _check("awq_gptq_hessian", lib().awq_gptq_hessian(
         _dev(X, "X"), _dtype_code(X), T, n_in, float(damp), _dev(H, "H", torch.float64), _stream()))
     return H
@@ -344,7 +378,9 @@ def gptq_hessian(X, damp=0.01, H=None):
 def gptq_factor(H, U=None, workspace=None):
     """U (in, in) fp64, upper, with H^-1 = U^T U."""
     n_in = H.shape[0]
+    _need(H, "H", (n_in, n_in))
     U = torch.empty_like(H) if U is None else U
+    _need(U, "U", (n_in, n_in))
     ws = _workspace(int(lib().awq_gptq_factor_workspace_size(n_in)), H.device, workspace)
     _check("awq_gptq_factor", lib().awq_gptq_factor(
         _dev(H, "H", torch.float64), n_in, _dev(U, "U", torch.float64), _dev(ws, "workspace"),
@@ -355,6 +391,7 @@ def gptq_factor(H, U=None, workspace=None):
 def gptq_quantize(W, U, bits, group, mode, workspace=None):
     """The column loop on W with U; returns (qweight, scales, zeros)."""
     out, n_in = W.shape
+    _need(U, "U", (n_in, n_in))
     q, sc, z = _packed_outputs(out, n_in, bits, group, W.device)
     ws = _workspace(int(lib().awq_gptq_quantize_workspace_size(out, n_in)), W.device, workspace)
     _check("awq_gptq_quantize", lib().awq_gptq_quantize(

@@ -4,13 +4,18 @@ Bars:
   * H = 2 X^T X (damped): within the fp64 rounding of the sums,
     |dH| <= (T + 8) 2^-53 (2 sum_t |x_ti x_tj|) + damping rounding;
   * U: upper triangular, U^T U H = I to 1e-9, and equal to the oracle's
-    factor (numpy inverse and Cholesky) to 1e-9 relative;
+    factor (successive inverse-Hessian eliminations) to 1e-9 relative;
   * the column loop given the same U: codes, scales and zeros equal to the
     oracle's (both evaluate the same fp64 operations per element, only the
     order of the compensation sums differs);
-  * end to end: codes equal to the oracle's for all but rare rows where a
-    weight lies within rounding noise of a decision boundary, and the
-    calibration error equal to 1e-9 relative.
+  * end to end (the GPU factors H itself, so its U differs from the
+    oracle's in the last bits): codes, scales and zeros equal to the
+    oracle's in every row, except a row whose first difference is a near
+    tie: a code whose weight, as the oracle had corrected it, lies within
+    1e-9 (in quantization steps) of a rounding midpoint, or a scale one fp32
+    ulp apart (two fp64 values a few ulps apart that round to different fp32
+    values straddle a rounding boundary), or a zero one apart under equal
+    scales; the calibration error equal to 1e-9 relative when no row differs.
 Each test prints the case it runs (flushed) before touching the GPU.
 """
 import sys
@@ -59,6 +64,31 @@ def unpack(q, n_in, bits):
     return codes
 
 
+def unexplained_rows(codes, sc, z, codes_o, sc_o, z_o, Wfix_o, group, tol=1e-9):
+    """Rows where the GPU and the oracle disagree on a code, scale or zero, and
+    the rows among them whose first difference is not a near tie."""
+    differ = (codes != codes_o).any(1) | (sc != sc_o).any(1) | (z != z_o).any(1)
+    bad = []
+    for r in np.flatnonzero(differ):
+        c = np.flatnonzero(codes[r] != codes_o[r])
+        g = np.flatnonzero((sc[r] != sc_o[r]) | (z[r] != z_o[r]))
+        first_code = int(c[0]) if c.size else None
+        first_group = int(g[0]) if g.size else None
+        if first_group is not None and (first_code is None or first_group * group <= first_code):
+            a, b = np.float32(sc[r, first_group]), np.float32(sc_o[r, first_group])
+            one_ulp = a == b or np.nextafter(a, b) == b
+            zero_step = abs(int(z[r, first_group]) - int(z_o[r, first_group])) <= (0 if a != b else 1)
+            if not (one_ulp and (a != b or zero_step)):
+                bad.append(int(r))
+            continue
+        i = first_code
+        t = Wfix_o[r, i] / float(sc_o[r, i // group])
+        frac = abs(t - np.floor(t) - 0.5)
+        if frac > tol * max(1.0, abs(t)):
+            bad.append(int(r))
+    return int(differ.sum()), bad
+
+
 def dequant(codes, sc, z, group):
     return np.repeat(sc.astype(np.float64), group, 1) * (codes - np.repeat(z.astype(np.float64), group, 1))
 
@@ -82,7 +112,7 @@ def test_factor(awq, ref, n_in, T):
     U = awq.gptq_factor(torch.from_numpy(H).cuda()).cpu().numpy()
     assert np.all(np.tril(U, -1) == 0.0)
     np.testing.assert_allclose(U.T @ U @ H, np.eye(n_in), rtol=0, atol=1e-9)
-    Uo = G.inverse_cholesky_upper(H)
+    Uo = G.obs_factor(H)
     assert np.abs(U - Uo).max() <= 1e-9 * np.abs(Uo).max()
 
 
@@ -105,7 +135,7 @@ QCASES = [
 def test_column_loop_matches_oracle(awq, ref, case):
     dt, mode, bits, group, out, n_in, T = QCASES[case]
     Ws, _, W32, X32 = make(out, n_in, T, dt, 10 + case)
-    U = G.inverse_cholesky_upper(G.dampen(G.hessian(X32), 0.01))
+    U = G.obs_factor(G.dampen(G.hessian(X32), 0.01))
     codes_o, sc_o, z_o, _ = G.gptq(W32, bits=bits, group=group, mode=mode, U=U)
     say("gptq column loop", QCASES[case])
     q, sc, z = awq.gptq_quantize(awq.to_device(Ws, dt), torch.from_numpy(np.ascontiguousarray(U)).cuda(),
@@ -121,15 +151,16 @@ def test_column_loop_matches_oracle(awq, ref, case):
 def test_gptq_end_to_end(awq, ref, case):
     dt, mode, bits, group, out, n_in, T = QCASES[case]
     Ws, Xs, W32, X32 = make(out, n_in, T, dt, 20 + case)
-    codes_o, sc_o, z_o, Wq_o = G.gptq(W32, X32, bits, group, mode)
+    codes_o, sc_o, z_o, Wq_o, Wfix_o = G.gptq(W32, X32, bits, group, mode, corrected=True)
     say("gptq end to end", QCASES[case])
     q, sc, z = awq.gptq(awq.to_device(Ws, dt), awq.to_device(Xs, dt), bits, group, mode)
     torch.cuda.synchronize()
     codes = unpack(q.cpu().numpy(), n_in, bits)
-    rows_differ = int((codes != codes_o).any(axis=1).sum())
-    say("rows differing", rows_differ, "of", out)
-    assert rows_differ <= max(1, out // 100)
-    Wq = dequant(codes, sc.cpu().numpy(), z.cpu().numpy(), group)
+    sc, z = sc.cpu().numpy(), z.cpu().numpy()
+    rows_differ, bad = unexplained_rows(codes, sc, z, codes_o, sc_o, z_o, Wfix_o, group)
+    say("rows differing", rows_differ, "of", out, "not at a near tie", bad)
+    assert not bad
+    Wq = dequant(codes, sc, z, group)
     e_gpu, e_o = G.output_sse(W32, Wq, X32), G.output_sse(W32, Wq_o, X32)
     assert abs(e_gpu - e_o) <= 1e-9 * e_o or rows_differ > 0
     # GPTQ's purpose: below RTN on the calibration data
@@ -148,17 +179,19 @@ def test_gptq_full_size_sampled_rows(awq, ref):
     q, sc, z = awq.gptq(Wd, Xd, 4, 128, "asym")
     torch.cuda.synchronize()
     X32 = synth.storage_to_f32(lay["X"], spec.dtype)
-    U = G.inverse_cholesky_upper(G.dampen(G.hessian(X32), 0.01))
+    # The oracle's factor by the library route (numpy's Cholesky of the
+    # inverse): at 4096 inputs the elimination form takes minutes, and the
+    # oracle's pins show the two agree.
+    U = np.linalg.cholesky(np.linalg.inv(G.dampen(G.hessian(X32), 0.01))).T
     rows = np.r_[0:16, 2040:2056, 4080:4096]
     W32 = synth.storage_to_f32(lay["W"][rows], spec.dtype)
-    codes_o, sc_o, z_o, Wq_o = G.gptq(W32, bits=4, group=128, mode="asym", U=U)
+    codes_o, sc_o, z_o, Wq_o, Wfix_o = G.gptq(W32, bits=4, group=128, mode="asym", U=U, corrected=True)
     codes = unpack(q.cpu().numpy()[rows], spec.inn, 4)
-    rows_differ = int((codes != codes_o).any(axis=1).sum())
-    say("full size rows differing", rows_differ, "of", len(rows))
-    assert rows_differ <= 2
-    same = ~(codes != codes_o).any(axis=1)
-    assert np.array_equal(sc.cpu().numpy()[rows][same], sc_o[same])
-    Wq = dequant(codes, sc.cpu().numpy()[rows], z.cpu().numpy()[rows], 128)
+    sc, z = sc.cpu().numpy()[rows], z.cpu().numpy()[rows]
+    rows_differ, bad = unexplained_rows(codes, sc, z, codes_o, sc_o, z_o, Wfix_o, 128)
+    say("full size rows differing", rows_differ, "of", len(rows), "not at a near tie", bad)
+    assert not bad
+    Wq = dequant(codes, sc, z, 128)
     e_gpu, e_o = G.output_sse(W32, Wq, X32), G.output_sse(W32, Wq_o, X32)
     say("full size sse gpu / oracle", e_gpu, e_o)
     assert abs(e_gpu - e_o) <= 1e-3 * e_o

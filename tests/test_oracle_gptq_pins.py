@@ -1,15 +1,18 @@
 """Pins of the GPTQ oracle (CPU only).
 
-The oracle follows "AWQ vs GPTQ Quantization Architectures Compared", "GPTQ:
-compensate the error you just made" step by step (Cholesky factor of the
-inverse Hessian, column-by-column rounding and compensation, lazily fitted
-group parameters). The pins tie it to facts that do not go through that
-route:
+The oracle states GPTQ as Optimal Brain Surgeon steps ("Advanced
+Quantization Algorithms: AWQ and GPTQ Explained", section 3; "AWQ vs GPTQ
+Quantization Architectures Compared", "GPTQ: compensate the error you just
+made"): weights fixed one at a time, the free ones moved by the row of the
+current inverse Hessian, that inverse updated by eliminating the fixed
+weight. The pins tie it to facts that do not go through that route:
   - the compensation is the exact least-squares correction: after the
     columns before j are fixed at their rounded values, the weights left free
     are the minimisers of ||X (W' - W)||^2 (the Optimal Brain Surgeon step the
     page starts from), computed here with a plain linear solve on H;
-  - a hand-worked two-column case;
+  - a hand-worked two-column case, and a hand-worked factor;
+  - the factor of the successive inverses is the upper Cholesky factor of
+    H^-1 (V^T V = H^-1, V upper), checked against the library's Cholesky;
   - with a diagonal Hessian there is nothing to compensate: the codes are the
     nearest levels of a brute-force search over every code;
   - GPTQ's output error on the calibration data is below RTN's on the
@@ -63,12 +66,25 @@ def test_dampening_hand_example():
     np.testing.assert_allclose(H, [[4.07, 2.0], [2.0, 10.07]], rtol=0, atol=1e-15)
 
 
-def test_inverse_cholesky_factor_hand_example():
-    # H = [[4, 2], [2, 10]]: H^-1 = [[10, -2], [-2, 4]] / 36; its lower Cholesky
-    # factor is [[sqrt(10)/6, 0], [-2/(6 sqrt(10)), sqrt(4/36 - 4/360)]]
-    U = G.inverse_cholesky_upper(np.array([[4.0, 2.0], [2.0, 10.0]]))
+def test_factor_hand_example():
+    # H = [[4, 2], [2, 10]]: H^-1 = [[10, -2], [-2, 4]] / 36. Row 0 is row 0 of
+    # H^-1 over sqrt(10/36); eliminating index 0 leaves 4/36 - (2/36)^2 / (10/36).
+    U = G.obs_factor(np.array([[4.0, 2.0], [2.0, 10.0]]))
     want = np.array([[np.sqrt(10) / 6, -2 / (6 * np.sqrt(10))], [0.0, np.sqrt(4 / 36 - 4 / 360)]])
     np.testing.assert_allclose(U, want, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,seed", [(5, 0), (33, 1), (128, 2)])
+def test_factor_is_the_cholesky_factor_of_the_inverse(n, seed):
+    r = np.random.default_rng(seed)
+    A = r.standard_normal((3 * n, n))
+    H = G.dampen(2.0 * A.T @ A, 0.01)
+    V = G.obs_factor(H)
+    assert np.all(np.tril(V, -1) == 0.0) and np.all(np.diag(V) > 0)
+    Hinv = np.linalg.inv(H)
+    np.testing.assert_allclose(V.T @ V, Hinv, rtol=0, atol=1e-10 * np.abs(Hinv).max())
+    # a library route to the same factor: Cholesky of H^-1, transposed
+    np.testing.assert_allclose(V, np.linalg.cholesky(Hinv).T, rtol=0, atol=1e-9 * np.abs(V).max())
 
 
 def test_hand_worked_two_columns():

@@ -81,14 +81,26 @@ def test_worked_example_two_channels(ref):
 # P2: alpha = 0 is plain RTN
 # ---------------------------------------------------------------------------
 def _torch_rtn(w, bits, group):
-    """Symmetric group RTN written with torch primitives, following the n-bit
-    RTN of the notebook's 'Output MSE vs bit width' section (fp32, no cast back)."""
+    """Symmetric group RTN ("Output MSE vs bit width" of "GPTQ and AWQ weight
+    quantisation") as a nearest-level search in torch: each group's step is
+    its largest magnitude over the 2^(b-1) - 1 positive levels (floored at
+    1e-8); every weight takes the level k in [-2^(b-1), 2^(b-1) - 1] nearest
+    to w / step (fp32 quotient, as the method computes it), ties to the even
+    k; the value is k * step in fp32."""
     out_f, in_f = w.shape
-    levels = (1 << (bits - 1)) - 1
-    wg = torch.from_numpy(w).view(out_f, in_f // group, group).float()
-    scale = (wg.abs().amax(dim=-1, keepdim=True) / levels).clamp(min=1e-8)
-    q = torch.round(wg / scale).clamp(-levels - 1, levels)
-    return (q * scale).view(out_f, in_f).numpy(), q.view(out_f, in_f).numpy().astype(np.int64)
+    top = (1 << (bits - 1)) - 1
+    wg = torch.from_numpy(w).reshape(out_f, in_f // group, group).to(torch.float32)
+    step = torch.maximum(wg.abs().max(dim=-1, keepdim=True).values / top,
+                         torch.tensor(1e-8, dtype=torch.float32))
+    t = (wg / step).to(torch.float64).unsqueeze(-1)          # exact in fp64
+    ks = torch.arange(-top - 1, top + 1, dtype=torch.float64)
+    dist = (t - ks).abs()
+    near = dist == dist.min(dim=-1, keepdim=True).values
+    # among equally near levels, the even one
+    pick = torch.where(near & (ks.remainder(2) == 0), 1, 0) + near.to(torch.int64) * 2
+    k = ks[pick.argmax(dim=-1)]
+    value = (k.to(torch.float32) * step)
+    return value.reshape(out_f, in_f).numpy(), k.reshape(out_f, in_f).numpy().astype(np.int64)
 
 
 @pytest.mark.parametrize("bits,group", [(4, 128), (3, 64), (2, 32)])
