@@ -1,8 +1,9 @@
 """Benchmark of the AWQ per-layer scale search and pack on one MI355X.
 
 One step = the whole path for one layer with its inputs resident in HBM:
-activation statistics, candidate scales, the fused error search over every
-alpha, the reduction and argmin, and the final quantize-and-pack. The workload
+activation statistics, candidate scales (with X's matrix-fragment copy in
+the same launch), the fused error search over every alpha, the reduction
+and argmin, and the final quantize-and-pack. The workload
 is the 4096x4096 fp16 linear layer with 256 calibration tokens, int4
 symmetric, group 128, grid 20 (21 alpha candidates), on seeded synthetic data.
 
@@ -424,21 +425,28 @@ def main():
 
     stages = ["stats", "prepare", "search", "finish", "pack"]
 
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record()
-        mark(0)
+    def step():
+        # The path as a user runs it: statistics, the single-call search
+        # (preparation with X's fragment copy, error kernel, finish), the
+        # pack -- five launches back to back.
         awq.act_stats(X, xmag, ws_s)
-        mark(1)
-        awq.search_prepare(xmag, out, T, grid, ws)
-        mark(2)
-        awq.search_candidates(W, X, spec.bits, spec.group, grid, spec.mode, ws)
-        mark(3)
-        awq.search_finish(out, n_in, T, grid, mse, best, s_best, ws)
-        mark(4)
+        awq.search(W, X, xmag, spec.bits, spec.group, grid, spec.mode, mse, best, s_best, ws)
         awq.quantize_pack(W, s_best, spec.bits, spec.group, spec.mode, qweight, scales, zeros)
-        mark(5)
+
+    def staged(ev):
+        # The same work as separate stages, one launch each, with events
+        # between them: the per-kernel times.
+        ev[0].record()
+        awq.act_stats(X, xmag, ws_s)
+        ev[1].record()
+        awq.search_prepare(X, xmag, out, grid, ws)
+        ev[2].record()
+        awq.search_candidates(W, X, spec.bits, spec.group, grid, spec.mode, ws)
+        ev[3].record()
+        awq.search_finish(out, n_in, T, grid, mse, best, s_best, ws)
+        ev[4].record()
+        awq.quantize_pack(W, s_best, spec.bits, spec.group, spec.mode, qweight, scales, zeros)
+        ev[5].record()
 
     for _ in range(args.warmup):
         step()
@@ -461,7 +469,7 @@ def main():
     # same K steps again with events between the stages.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for k in range(args.steps):
-        step(events[k])
+        staged(events[k])
     torch.cuda.synchronize()
     per = {s: [] for s in stages}
     for ev in events:

@@ -132,19 +132,22 @@ int awq_search_noalloc(const void *W, const void *X, int dtype, int64_t out, int
                        double *mse, int32_t *best, float *s_best, void *stream);
 
 /* awq_search in its three stages, in this order on one stream with one
- * workspace (awq_search is exactly the three calls). They let a caller time or
- * profile the error kernel alone, and they are where a search sharded over
- * devices would combine its partial sums. Arguments mean what they mean for
- * awq_search; each stage validates its own arguments the same way.
- *   awq_search_prepare:    the s-table and its reciprocals into ws (step 2).
+ * workspace. They let a caller time or profile the error kernel alone, and
+ * they are where a search sharded over devices would combine its partial
+ * sums. Arguments mean what they mean for awq_search; each stage validates
+ * its own arguments the same way.
+ *   awq_search_prepare:    the s-table and its reciprocals into ws (step 2),
+ *                          and, for layers that take the 16-bit search, a
+ *                          copy of X in matrix-fragment order (one launch).
  *   awq_search_candidates: the fused quantize-dequantize-error kernel; leaves
  *                          one fp64 partial sum of squares per (candidate,
  *                          block of 16 rows x 256 tokens) in ws. Needs the
- *                          prepared ws.
+ *                          ws that awq_search_prepare filled from the same X.
  *   awq_search_finish:     fixed-order reduction of the partials into mse,
- *                          argmin into best, s_best. Needs the candidates' ws. */
-int awq_search_prepare(const float *xmag, int64_t out, int64_t in, int64_t tokens, int grid,
-                       void *ws, size_t ws_bytes, void *stream);
+ *                          argmin into best, s_best. Needs the candidates' ws.
+ * awq_search is exactly the three stages. */
+int awq_search_prepare(const void *X, int dtype, const float *xmag, int64_t out, int64_t in,
+                       int64_t tokens, int grid, void *ws, size_t ws_bytes, void *stream);
 int awq_search_candidates(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                           int64_t tokens, int bits, int group, int grid, int mode, void *ws,
                           size_t ws_bytes, void *stream);

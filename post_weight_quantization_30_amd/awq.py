@@ -54,7 +54,7 @@ def lib():
         L.awq_search_noalloc.argtypes = [vp, vp, cint, i64, i64, i64, vp, cint, cint, cint, cint,
                                          vp, vp, vp, vp]
         L.awq_search_noalloc.restype = cint
-        L.awq_search_prepare.argtypes = [vp, i64, i64, i64, cint, vp, sz, vp]
+        L.awq_search_prepare.argtypes = [vp, cint, vp, i64, i64, i64, cint, vp, sz, vp]
         L.awq_search_prepare.restype = cint
         L.awq_search_candidates.argtypes = [vp, vp, cint, i64, i64, i64, cint, cint, cint, cint,
                                             vp, sz, vp]
@@ -221,9 +221,12 @@ def search_noalloc(W, X, xmag, bits, group, grid, mode, mse, best, s_best):
     return mse, best, s_best
 
 
-def search_prepare(xmag, out, tokens, grid, workspace):
+def search_prepare(X, xmag, out, grid, workspace):
+    """The s-table (and, for the 16-bit search, X in fragment order) into the workspace."""
+    T, n_in = X.shape
+    _need(xmag, "xmag", (n_in,))
     _check("awq_search_prepare", lib().awq_search_prepare(
-        _dev(xmag, "xmag", torch.float32), out, xmag.shape[0], tokens, grid,
+        _dev(X, "X"), _dtype_code(X), _dev(xmag, "xmag", torch.float32), out, n_in, T, grid,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
 
 

@@ -115,21 +115,23 @@ int check_candidates(const void *W, const void *X, int dtype, int64_t in, int bi
 
 }  // namespace
 
-int awq_search_prepare(const float *xmag, int64_t out, int64_t in, int64_t tokens, int grid,
-                       void *ws, size_t ws_bytes, void *stream)
+int awq_search_prepare(const void *X, int dtype, const float *xmag, int64_t out, int64_t in,
+                       int64_t tokens, int grid, void *ws, size_t ws_bytes, void *stream)
 {
-    if (!xmag)
+    if (!X || !xmag || !valid_dtype(dtype))
         return AWQ_ERR_INVALID_ARG;
     int st = check_search_shape(out, in, tokens, grid);
     awq::SearchWs lay;
     if (st == AWQ_OK)
         st = check_workspace(out, in, tokens, grid, ws, ws_bytes, &lay);
+    if (st == AWQ_OK && !aligned16(X))
+        st = AWQ_ERR_UNSUPPORTED;
     if (st != AWQ_OK)
         return st;
     char *base = (char *)ws;
-    return hip_status(awq::launch_s_table(xmag, in, grid, (float *)(base + lay.s_off),
-                                          (float *)(base + lay.inv_off),
-                                          (int32_t *)(base + lay.unit_off), (hipStream_t)stream));
+    return hip_status(awq::launch_prepare(X, dtype, xmag, out, in, tokens, grid, (float *)(base + lay.s_off),
+                                          (float *)(base + lay.inv_off), (int32_t *)(base + lay.unit_off),
+                                          base + lay.xf_off, (hipStream_t)stream));
 }
 
 int awq_search_candidates(const void *W, const void *X, int dtype, int64_t out, int64_t in,
@@ -151,7 +153,7 @@ int awq_search_candidates(const void *W, const void *X, int dtype, int64_t out, 
                                          (const float *)(base + lay.inv_off),
                                          (const int32_t *)(base + lay.unit_off), grid + 1, bits,
                                          group, mode, (double *)(base + lay.part_off),
-                                         base + lay.xf_off, (hipStream_t)stream));
+                                         base + lay.xf_off, nullptr, (hipStream_t)stream));
 }
 
 int awq_search_finish(int64_t out, int64_t in, int64_t tokens, int grid, double *mse,
@@ -172,11 +174,13 @@ int awq_search_finish(int64_t out, int64_t in, int64_t tokens, int grid, double 
                                                 s_best, (hipStream_t)stream));
 }
 
+// The single call: the three stages, validated together up front and
+// enqueued back to back.
 int awq_search(const void *W, const void *X, int dtype, int64_t out, int64_t in, int64_t tokens,
                const float *xmag, int bits, int group, int grid, int mode, double *mse,
                int32_t *best, float *s_best, void *ws, size_t ws_bytes, void *stream)
 {
-    // Validate everything for all three stages before the first launch.
+    // Validate everything for all stages before the first launch.
     if (!xmag || !mse || !best || !s_best)
         return AWQ_ERR_INVALID_ARG;
     int st = check_candidates(W, X, dtype, in, bits, group, mode);
@@ -189,13 +193,16 @@ int awq_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
         st = AWQ_ERR_UNSUPPORTED;
     if (st != AWQ_OK)
         return st;
-    st = awq_search_prepare(xmag, out, in, tokens, grid, ws, ws_bytes, stream);
-    if (st == AWQ_OK)
-        st = awq_search_candidates(W, X, dtype, out, in, tokens, bits, group, grid, mode, ws,
-                                   ws_bytes, stream);
-    if (st == AWQ_OK)
-        st = awq_search_finish(out, in, tokens, grid, mse, best, s_best, ws, ws_bytes, stream);
-    return st;
+    st = awq_search_prepare(X, dtype, xmag, out, in, tokens, grid, ws, ws_bytes, stream);
+    if (st != AWQ_OK)
+        return st;
+    char *base = (char *)ws;
+    const awq::FinishOut fin{mse, best, s_best};
+    return hip_status(awq::launch_search(W, X, dtype, out, in, tokens, (const float *)(base + lay.s_off),
+                                         (const float *)(base + lay.inv_off),
+                                         (const int32_t *)(base + lay.unit_off), grid + 1, bits,
+                                         group, mode, (double *)(base + lay.part_off),
+                                         base + lay.xf_off, &fin, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -586,12 +586,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search(
     }
 }
 
-// The finish: fixed-order reduction of the block partials of every candidate
-// (wave w takes candidates w, w + 16, ...; lane l sums partials l, l + 64, ...
-// in order, then a fixed xor butterfly), then the first strict minimum over
-// the candidates (a NaN never compares below) and s_best = that row of the
-// s-table, or all ones when nothing is finite. One block: the work is a few
-// thousand doubles for the layers this is meant for.
+// The finish as its own launch (one block; the work is a few thousand
+// doubles for the layers this is meant for). Body: finish_block.
 constexpr int kFinishWaves = 16;
 
 __global__ __launch_bounds__(kFinishWaves * 64) void k_finish(const double *__restrict__ partial,
@@ -603,59 +599,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_finish(const double *__re
 {
     __shared__ double err[AWQ_MAX_GRID + 1];
     __shared__ int sbest;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int a = wave; a < n_alpha; a += kFinishWaves) {
-        const double *p = partial + (int64_t)a * nblk;
-        double acc = 0.0;
-        int64_t b = lane;
-        for (; b + 192 < nblk; b += 256) {
-            const double x0 = p[b], x1 = p[b + 64], x2 = p[b + 128], x3 = p[b + 192];
-            acc += x0;
-            acc += x1;
-            acc += x2;
-            acc += x3;
-        }
-        for (; b < nblk; b += 64)
-            acc += p[b];
-        for (int off = 32; off > 0; off >>= 1)
-            acc += __shfl_xor(acc, off);
-        if (lane == 0) {
-            const double m = acc / denom;
-            err[a] = m;
-            mse[a] = m;
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int bi = -1;
-        double be = INFINITY;
-        for (int k = 0; k < n_alpha; ++k) {
-            if (err[k] < be) {
-                be = err[k];
-                bi = k;
-            }
-        }
-        sbest = bi;
-        *best = bi;
-    }
-    __syncthreads();
-    const int bi = sbest;
-    const float *src = s_tab + (int64_t)(bi >= 0 ? bi : 0) * in;
-    // four independent loads in flight per thread per round
-    for (int64_t j0 = threadIdx.x; j0 < in; j0 += 4 * (int64_t)blockDim.x) {
-        float x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t j = j0 + u * (int64_t)blockDim.x;
-            x[u] = bi >= 0 && j < in ? src[j] : 1.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t j = j0 + u * (int64_t)blockDim.x;
-            if (j < in)
-                s_best[j] = x[u];
-        }
-    }
+    finish_block(partial, nblk, n_alpha, denom, s_tab, in, mse, best, s_best, err, &sbest);
 }
 
 template <typename TIn, typename TOp, int G>
@@ -708,47 +652,63 @@ bool search_uses_fp32_operands(int dtype, int64_t out, int64_t tokens)
 
 // The 32x32 search (k_search16.hip) takes 16-bit operands with `in` a
 // multiple of 128 and passes of 9..12 candidates (n_alpha >= 9).
-bool search16_applies(int64_t in, int n_alpha, int64_t nblocks)
+bool search16_applies(int dtype, int64_t out, int64_t in, int64_t tokens, int n_alpha)
 {
+    if (search_uses_fp32_operands(dtype, out, tokens))
+        return false;
     const int npass = (n_alpha + 11) / 12;
+    const int64_t nblocks = ((out + 15) / 16) * ((tokens + kTokPerBlock - 1) / kTokPerBlock);
     return in % 128 == 0 && n_alpha / npass >= 9 && nblocks * npass <= 0x7fffffffLL;
 }
 
-hipError_t launch_search16(const void *W, const void *X, int dtype, int64_t out, int64_t in,
-                           int64_t tokens, const float *s_tab, const float *inv_tab,
-                           const int32_t *unit, int n_alpha, int bits, int group, int mode,
-                           double *partial, void *xfrag, hipStream_t st)
+hipError_t launch_prepare(const void *X, int dtype, const float *xmag, int64_t out, int64_t in,
+                          int64_t tokens, int grid, float *s_tab, float *inv_tab, int32_t *unit,
+                          void *xfrag, hipStream_t st)
 {
-#define AWQ_S16_CALL(name) name(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, mode, partial, xfrag, st)
-    if (dtype == AWQ_F16)
-        return group == 32 ? AWQ_S16_CALL(launch_search16_f16_g32)
-             : group == 64 ? AWQ_S16_CALL(launch_search16_f16_g64)
-                           : AWQ_S16_CALL(launch_search16_f16_g128);
-    return group == 32 ? AWQ_S16_CALL(launch_search16_bf16_g32)
-         : group == 64 ? AWQ_S16_CALL(launch_search16_bf16_g64)
-                       : AWQ_S16_CALL(launch_search16_bf16_g128);
-#undef AWQ_S16_CALL
+    if (search16_applies(dtype, out, in, tokens, grid + 1))
+        return dtype == AWQ_F16 ? launch_prepare16_f16(X, xmag, in, tokens, grid, s_tab, inv_tab, unit, xfrag, st)
+                                : launch_prepare16_bf16(X, xmag, in, tokens, grid, s_tab, inv_tab, unit, xfrag, st);
+    return launch_s_table(xmag, in, grid, s_tab, inv_tab, unit, st);
 }
 
 hipError_t launch_search(const void *W, const void *X, int dtype, int64_t out, int64_t in,
                          int64_t tokens, const float *s_tab, const float *inv_tab,
                          const int32_t *unit, int n_alpha, int bits, int group, int mode,
-                         double *partial, void *xfrag, hipStream_t st)
+                         double *partial, const void *xfrag, const FinishOut *fin, hipStream_t st)
 {
+    hipError_t e;
     const bool wide = search_uses_fp32_operands(dtype, out, tokens);
-    if (!wide && search16_applies(in, n_alpha, ((out + 15) / 16) * ((tokens + kTokPerBlock - 1) / kTokPerBlock)))
-        return launch_search16(W, X, dtype, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group,
-                               mode, partial, xfrag, st);
-    switch (dtype) {
-    case AWQ_F32:
-        return search_group<float, float>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st);
-    case AWQ_F16:
-        return wide ? search_group<f16, float>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st)
-                    : search_group<f16, f16>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st);
-    default:
-        return wide ? search_group<bf16, float>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st)
-                    : search_group<bf16, bf16>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st);
+    if (search16_applies(dtype, out, in, tokens, n_alpha)) {
+#define AWQ_S16_CALL(name) name(W, xfrag, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, mode, partial, st)
+        if (dtype == AWQ_F16)
+            e = group == 32 ? AWQ_S16_CALL(launch_search16_f16_g32)
+              : group == 64 ? AWQ_S16_CALL(launch_search16_f16_g64)
+                            : AWQ_S16_CALL(launch_search16_f16_g128);
+        else
+            e = group == 32 ? AWQ_S16_CALL(launch_search16_bf16_g32)
+              : group == 64 ? AWQ_S16_CALL(launch_search16_bf16_g64)
+                            : AWQ_S16_CALL(launch_search16_bf16_g128);
+#undef AWQ_S16_CALL
+    } else {
+        switch (dtype) {
+        case AWQ_F32:
+            e = search_group<float, float>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st);
+            break;
+        case AWQ_F16:
+            e = wide ? search_group<f16, float>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st)
+                     : search_group<f16, f16>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st);
+            break;
+        default:
+            e = wide ? search_group<bf16, float>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st)
+                     : search_group<bf16, bf16>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha, bits, group, mode, partial, st);
+            break;
+        }
     }
+    // single-call search: the finish follows on the same stream
+    if (e == hipSuccess && fin)
+        e = launch_reduce_argmin(partial, ((out + 15) / 16) * ((tokens + kTokPerBlock - 1) / kTokPerBlock),
+                                 n_alpha, out, tokens, in, s_tab, fin->mse, fin->best, fin->s_best, st);
+    return e;
 }
 
 hipError_t launch_reduce_argmin(const double *partial, int64_t nblk, int n_alpha, int64_t out,

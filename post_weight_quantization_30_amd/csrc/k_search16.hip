@@ -672,12 +672,12 @@ struct Search {
 // si) * 8 + w) * 8 + s) * 64 + l holds, for token tb*256 + 32w + (l & 31) and
 // input columns 128 si + 64 (l >> 5) + 8s .. + 7, the 8 stored values (zero
 // past the last token). One thread per fragment; the writes are contiguous.
+// Written by the preparation kernel below.
 template <typename T>
-__global__ __launch_bounds__(256) void k_xfrag(const T *__restrict__ X, int64_t tokens, int64_t in,
-                                               int64_t nfrag, typename Vec8<T>::type *__restrict__ xf)
+__device__ __forceinline__ void xfrag_one(const T *__restrict__ X, int64_t tokens, int64_t in, int64_t nfrag,
+                                          typename Vec8<T>::type *__restrict__ xf, int64_t f)
 {
     typedef typename Vec8<T>::type V8;
-    const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (f >= nfrag)
         return;
     const int64_t nsteps = in / kStep;
@@ -747,18 +747,46 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search16(
 #undef AWQ_S16_RUN
 }
 
+// Preparation in one launch: blocks [0, nS) compute the s-table (one per
+// 256 columns and candidate), blocks from nS on write the fragment-ordered
+// copy of X (one thread per fragment).
+template <typename T>
+__global__ __launch_bounds__(256) void k_prepare16(const T *__restrict__ X, int64_t tokens, int64_t in,
+                                                   int64_t nfrag, typename Vec8<T>::type *__restrict__ xf,
+                                                   const float *__restrict__ xmag, int grid,
+                                                   float *__restrict__ s_tab, float *__restrict__ inv_tab,
+                                                   int32_t *__restrict__ unit, int64_t ncb)
+{
+    const int64_t b = blockIdx.x, nS = ncb * (grid + 1);
+    if (b < nS) {
+        s_table_block(xmag, in, grid, (int)(b / ncb), b % ncb, s_tab, inv_tab, unit);
+        return;
+    }
+    xfrag_one<T>(X, tokens, in, nfrag, xf, (b - nS) * 256 + threadIdx.x);
+}
+
+template <typename T>
+static hipError_t launch_prepare_typed(const void *X, const float *xmag, int64_t in, int64_t tokens,
+                                       int grid, float *s_tab, float *inv_tab, int32_t *unit, void *xfrag,
+                                       hipStream_t st)
+{
+    const int64_t ntb = (tokens + kTokPerBlock - 1) / kTokPerBlock;
+    const int64_t nfrag = ntb * kTokPerBlock * in / 8;
+    const int64_t ncb = (in + 255) / 256;
+    const int64_t nblocks = ncb * (grid + 1) + (nfrag + 255) / 256;
+    hipLaunchKernelGGL((k_prepare16<T>), dim3((unsigned)nblocks), dim3(256), 0, st, (const T *)X, tokens, in,
+                       nfrag, (typename Vec8<T>::type *)xfrag, xmag, grid, s_tab, inv_tab, unit, ncb);
+    return hipGetLastError();
+}
+
 template <typename T, int G>
-static hipError_t launch_typed(const void *W, const void *X, int64_t out, int64_t in, int64_t tokens,
+static hipError_t launch_typed(const void *W, const void *xfrag, int64_t out, int64_t in, int64_t tokens,
                                const float *s_tab, const float *inv_tab, const int32_t *unit,
-                               int n_alpha, int bits, int mode, double *partial, void *xfrag,
-                               hipStream_t st)
+                               int n_alpha, int bits, int mode, double *partial, hipStream_t st)
 {
     const int npass = (n_alpha + kSlots - 1) / kSlots;
     const int64_t nrb = (out + kRows - 1) / kRows;
     const int64_t ntb = (tokens + kTokPerBlock - 1) / kTokPerBlock;
-    const int64_t nfrag = ntb * kTokPerBlock * in / 8;
-    hipLaunchKernelGGL((k_xfrag<T>), dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0, st,
-                       (const T *)X, tokens, in, nfrag, (typename Vec8<T>::type *)xfrag);
     const dim3 grid((unsigned)(nrb * ntb * npass));
     const int q = n_alpha / npass, rem = n_alpha % npass;
     if (mode == AWQ_SYM)
@@ -783,11 +811,21 @@ static hipError_t launch_typed(const void *W, const void *X, int64_t out, int64_
 hipError_t AWQ_S16_CAT(launch_search16_, AWQ_S16_T, AWQ_S16_G)(
     const void *W, const void *X, int64_t out, int64_t in, int64_t tokens, const float *s_tab,
     const float *inv_tab, const int32_t *unit, int n_alpha, int bits, int mode, double *partial,
-    void *xfrag, hipStream_t st)
+    hipStream_t st)
 {
     return s16::launch_typed<AWQ_S16_T, AWQ_S16_G>(W, X, out, in, tokens, s_tab, inv_tab, unit, n_alpha,
-                                                   bits, mode, partial, xfrag, st);
+                                                   bits, mode, partial, st);
 }
+#if AWQ_S16_G == 128
+#define AWQ_S16_CAT1(a, b) a##b
+#define AWQ_S16_PREP(a, b) AWQ_S16_CAT1(a, b)
+hipError_t AWQ_S16_PREP(launch_prepare16_, AWQ_S16_T)(const void *X, const float *xmag, int64_t in,
+                                                       int64_t tokens, int grid, float *s_tab, float *inv_tab,
+                                                       int32_t *unit, void *xfrag, hipStream_t st)
+{
+    return s16::launch_prepare_typed<AWQ_S16_T>(X, xmag, in, tokens, grid, s_tab, inv_tab, unit, xfrag, st);
+}
+#endif
 #endif
 
 }  // namespace awq

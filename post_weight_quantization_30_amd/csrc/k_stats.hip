@@ -91,68 +91,14 @@ hipError_t launch_act_stats(const void *X, int dtype, int64_t tokens, int64_t in
     }
 }
 
-// One block per (256 columns, candidate k). For alpha >= 0, x -> x^alpha is
-// non-decreasing, and the fp32 inputs are at least one fp32 ulp (2^-23
-// relative) apart, far more than any error of an fp64 pow, so
-//   max_j pow(x_j, alpha) == pow(max_j x_j, alpha)   (and likewise for min)
-// holds for the computed values too: every block finds max and min of xmag
-// itself (exact, any order) and powers only those two and its own columns.
-// unit[k] is set when the two powers are equal (k = 0, or flat activations):
-// then every s is exactly 1 (sqrt(p * p) == p in binary floating point) and
-// the search treats the candidate's scaled weights as the raw stored values.
+// One block per (256 columns, candidate k); the body (s_table_block) is
+// shared with the preparation kernel of the 16-bit search.
 __global__ __launch_bounds__(256) void k_s_table(const float *__restrict__ xmag, int64_t in, int grid,
                                                   float *__restrict__ s_tab,
                                                   float *__restrict__ inv_tab,
                                                   int32_t *__restrict__ unit)
 {
-    __shared__ float smax[4], smin[4];
-    __shared__ double ext[2];
-    const int k = blockIdx.y;
-    const double alpha = (double)k / (double)grid;
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const bool col_ok = j < in;
-    const double p = pow((double)xmag[col_ok ? j : 0], alpha);
-
-    // Max and min of xmag (> 0): 16 independent loads in flight per thread
-    // per round (one round for in <= 4096).
-    float lmax = 0.f, lmin = FLT_MAX;
-    for (int64_t i0 = threadIdx.x; i0 < in; i0 += 256 * 16) {
-        float x[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int64_t i = i0 + 256 * u;
-            x[u] = xmag[i < in ? i : i0];
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            lmax = fmaxf(lmax, x[u]);
-            lmin = fminf(lmin, x[u]);
-        }
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-        lmax = fmaxf(lmax, __shfl_xor(lmax, off));
-        lmin = fminf(lmin, __shfl_xor(lmin, off));
-    }
-    if ((threadIdx.x & 63) == 0) {
-        smax[threadIdx.x >> 6] = lmax;
-        smin[threadIdx.x >> 6] = lmin;
-    }
-    __syncthreads();
-    if (threadIdx.x < 2) {
-        const float xm = threadIdx.x == 0 ? fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]))
-                                          : fminf(fminf(smin[0], smin[1]), fminf(smin[2], smin[3]));
-        ext[threadIdx.x] = pow((double)xm, alpha);
-    }
-    __syncthreads();
-    const double pmax = ext[0], pmin = ext[1];
-    if (unit && blockIdx.x == 0 && threadIdx.x == 0)
-        unit[k] = pmax == pmin ? 1 : 0;
-    if (!col_ok)
-        return;
-    const float s = (float)(p / sqrt(pmax * pmin));
-    s_tab[(int64_t)k * in + j] = s;
-    if (inv_tab)
-        inv_tab[(int64_t)k * in + j] = 1.0f / s;
+    s_table_block(xmag, in, grid, (int)blockIdx.y, (int64_t)blockIdx.x, s_tab, inv_tab, unit);
 }
 
 hipError_t launch_s_table(const float *xmag, int64_t in, int grid, float *s_tab, float *inv_tab,

@@ -241,7 +241,8 @@ def test_vector_kernels_reject_misaligned_pointers(L):
     for W, X, w in ((odd, FAKE, FAKE), (FAKE, odd, FAKE), (FAKE, FAKE, odd)):
         assert L.awq_search(W, X, 1, 64, 256, 32, FAKE, 4, 128, 20, 0, FAKE, FAKE, FAKE, w, ws, None) == -5
     assert L.awq_search_candidates(odd, FAKE, 1, 64, 256, 32, 4, 128, 20, 0, FAKE, ws, None) == -5
-    assert L.awq_search_prepare(FAKE, 64, 256, 32, 20, odd, ws, None) == -5
+    assert L.awq_search_prepare(FAKE, 1, FAKE, 64, 256, 32, 20, odd, ws, None) == -5
+    assert L.awq_search_prepare(odd, 1, FAKE, 64, 256, 32, 20, FAKE, ws, None) == -5
     assert L.awq_search_finish(64, 256, 32, 20, FAKE, FAKE, FAKE, odd, ws, None) == -5
     # clipping search: W, X
     assert L.awq_clip_search(odd, FAKE, 1, 64, 256, 32, FAKE, 4, 128, 0, 20, f(0.5), FAKE, None, None) == -5

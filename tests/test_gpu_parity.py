@@ -174,6 +174,29 @@ def test_search_is_deterministic(awq, ref):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("base,out,n_in,T", [(1, 512, 1024, 300), (2, 256, 512, 64), (0, 72, 256, 32)])
+def test_single_call_equals_stages(awq, ref, base, out, n_in, T):
+    """awq_search and its three stage calls (preparation with X's fragment
+    copy, error kernel, finish) give bitwise the same results, on the fp16
+    path, the bf16 asymmetric path and the fp32-operand path."""
+    spec = synth.with_shape(synth.CONFIGS[base], out=out, inn=n_in, tokens=T)
+    lay = synth.make_layer(spec)
+    say("single call vs stages", spec)
+    Wd, Xd = dev(lay["W"], spec.dtype), dev(lay["X"], spec.dtype)
+    xm = awq.act_stats(Xd)
+    a = [t.clone() for t in awq.search(Wd, Xd, xm, spec.bits, spec.group, spec.grid, spec.mode)]
+    ws = torch.empty(awq.search_workspace_size(out, n_in, T, spec.grid), dtype=torch.uint8, device="cuda")
+    mse = torch.empty(spec.grid + 1, dtype=torch.float64, device="cuda")
+    best = torch.empty(1, dtype=torch.int32, device="cuda")
+    sb = torch.empty(n_in, dtype=torch.float32, device="cuda")
+    awq.search_prepare(Xd, xm, out, spec.grid, ws)
+    awq.search_candidates(Wd, Xd, spec.bits, spec.group, spec.grid, spec.mode, ws)
+    awq.search_finish(out, n_in, T, spec.grid, mse, best, sb, ws)
+    torch.cuda.synchronize()
+    for x, y in zip(a, (mse, best, sb)):
+        assert torch.equal(x, y)
+
+
 def test_flat_activations_choose_rtn(awq, ref):
     r = np.random.default_rng(3)
     W = (r.standard_normal((32, 256)) * 0.02).astype(np.float16)
