@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--no-clip", action="store_true",
                    help="skip the clipping-range search measurement")
     p.add_argument("--no-gptq", action="store_true", help="skip the GPTQ measurement")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-workload records of the other layers")
     p.add_argument("--clip-steps", type=int, default=10,
                    help="timed launches of the clipping-range search")
     return p.parse_args()
@@ -392,23 +394,12 @@ def gptq_measure(awq, torch, spec, W, X, xmag_mse, args, awq_pack=None):
             "heldout_mse": held}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the AWQ search of one layer is measured on a "
-              "single MI355X; several GPUs would each search their own rows of the layer "
-              "(the row blocks are independent), which this measurement does not run.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    probe = None if args.no_mfma_peak else measured_mfma_peak()
-
-    import torch
-    from post_weight_quantization_30_amd import awq, synth
-
-    spec = synth.BY_NAME[args.config]
+def measure_layer(awq, torch, synth, spec, steps, warmup, probe, cold_reps=5):
+    """One workload: `steps` whole-path steps back to back (statistics, the
+    single-call search, the pack), the same work again as separate stages with
+    events between them, and cold-cache statistics and pack. Returns the
+    record and the tensors the other measurements reuse."""
     lay = synth.make_layer(spec)
-    torch.cuda.set_device(0)
     W = awq.to_device(lay["W"], spec.dtype)
     X = awq.to_device(lay["X"], spec.dtype)
     out, n_in, T, grid = spec.out, spec.inn, spec.tokens, spec.grid
@@ -448,7 +439,7 @@ def main():
         awq.quantize_pack(W, s_best, spec.bits, spec.group, spec.mode, qweight, scales, zeros)
         ev[5].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
@@ -458,17 +449,17 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / steps
 
     # Stage breakdown (and the search kernel's time for the roofline): the
     # same K steps again with events between the stages.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for k in range(args.steps):
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for k in range(steps):
         staged(events[k])
     torch.cuda.synchronize()
     per = {s: [] for s in stages}
@@ -481,7 +472,7 @@ def main():
     # evicts X and W from the 256 MiB Infinity Cache.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = {"stats": [], "pack": []}
-    for r in range(5):
+    for r in range(cold_reps):
         for name, fn in (("stats", lambda: awq.act_stats(X, xmag, ws_s)),
                          ("pack", lambda: awq.quantize_pack(W, s_best, spec.bits, spec.group, spec.mode,
                                                             qweight, scales, zeros))):
@@ -496,7 +487,6 @@ def main():
     cold_ms = {k: sorted(v)[len(v) // 2] for k, v in cold.items()}
 
     alpha_macs = spec.alpha_macs
-    value = alpha_macs / (ms_per_step * 1e-3)
     search_flops = 2.0 * alpha_macs
     fp32_ops = spec.dtype == "f32" or out < 256 or T < 16
     peak = PEAK_F32_TFLOPS if fp32_ops else PEAK_F16_TFLOPS
@@ -507,39 +497,97 @@ def main():
     esize = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
     stats_bytes = T * n_in * esize + 4 * n_in
     pack_bytes = out * n_in * esize + 4 * n_in + out * n_in * spec.bits / 8 + 5 * out * (n_in // spec.group)
-
     m = mse.cpu().numpy()
     b = int(best.item())
+    core = {
+        "ms_per_layer": ms_per_step,
+        "wall_ms_per_layer": wall * 1e3 / steps,
+        "alpha_macs_per_s": alpha_macs / (ms_per_step * 1e-3),
+        "stages_ms": avg,
+        "search_alpha_macs_per_s": alpha_macs / (avg["search"] * 1e-3),
+        "roofline": {"bound": "mfma", "kernel": "k_search16" if not fp32_ops else "k_search",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "peak_measured": measured,
+                     "frac_of_measured": achieved / measured if measured else None},
+        "stats_gbs": stats_bytes / (avg["stats"] * 1e-3) / 1e9,
+        "pack_gbs": pack_bytes / (avg["pack"] * 1e-3) / 1e9,
+        "stats_gbs_cold": stats_bytes / (cold_ms["stats"] * 1e-3) / 1e9,
+        "pack_gbs_cold": pack_bytes / (cold_ms["pack"] * 1e-3) / 1e9,
+        "result": {"best_index": b, "best_alpha": b / grid if b >= 0 else None,
+                   "awq_mse": float(m[b]) if b >= 0 else None, "rtn_mse": float(m[0])},
+    }
+    tensors = {"lay": lay, "W": W, "X": X, "xmag": xmag, "s_best": s_best, "qweight": qweight,
+               "scales": scales, "zeros": zeros, "mse": m, "best": b}
+    return core, tensors
+
+
+def oracle_rate(spec, lay, rows):
+    """The oracle on the first `rows` rows of the layer: the statistics over
+    all of X (timed on their own), then the search and the pack of those
+    rows; the alpha-candidate MAC/s of the search and pack, and the whole
+    layer's oracle time at that rate plus the statistics."""
+    from oracle import oracle as ref
+    from post_weight_quantization_30_amd import synth
+    Xf = synth.storage_to_f32(lay["X"], spec.dtype)
+    Wf = synth.storage_to_f32(lay["W"][:rows], spec.dtype)
+    t0 = time.perf_counter()
+    xmag = ref.act_stats(Xf)
+    t1 = time.perf_counter()
+    _, _, s_best, _ = ref.search(Wf, Xf, xmag, spec.bits, spec.group, spec.grid, spec.mode)
+    ref.quantize_pack(Wf, s_best, spec.bits, spec.group, spec.mode)
+    dt = time.perf_counter() - t1
+    rate = spec.n_alpha * spec.tokens * rows * spec.inn / dt
+    return {"alpha_macs_per_s": rate, "rows": rows, "stats_seconds": t1 - t0, "search_pack_seconds": dt,
+            "layer_seconds_at_rate": (t1 - t0) + spec.alpha_macs / rate}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the AWQ search of one layer is measured on a "
+              "single MI355X; several GPUs would each search their own rows of the layer "
+              "(the row blocks are independent), which this measurement does not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    probe = None if args.no_mfma_peak else measured_mfma_peak()
+
+    import torch
+    from post_weight_quantization_30_amd import awq, synth
+
+    spec = synth.BY_NAME[args.config]
+    torch.cuda.set_device(0)
+    core, t = measure_layer(awq, torch, synth, spec, args.steps, args.warmup, probe)
+    lay, W, X, xmag, s_best, qweight, scales, zeros, m, b = (t[k] for k in (
+        "lay", "W", "X", "xmag", "s_best", "qweight", "scales", "zeros", "mse", "best"))
+    dev = W.device
+    grid = spec.grid
     rec = {
         "metric": METRIC,
-        "value": value,
+        "value": core["alpha_macs_per_s"],
         "unit": "alpha-candidate MAC/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": core["ms_per_layer"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16" if spec.dtype == "f16" else spec.dtype,
         "data": "synthetic",
-        "config": {"workload": spec.name, "out": out, "in": n_in, "tokens": T, "bits": spec.bits,
-                   "group": spec.group, "mode": spec.mode, "n_alpha": spec.n_alpha,
+        "config": {"workload": spec.name, "out": spec.out, "in": spec.inn, "tokens": spec.tokens,
+                   "bits": spec.bits, "group": spec.group, "mode": spec.mode, "n_alpha": spec.n_alpha,
                    "input_dtype": spec.dtype, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "k_search", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic_from_profile(spec.name),
-                     "peak_measured": measured, "frac_of_measured": achieved / measured if measured else None},
-        "stages_ms": avg,
-        "search_alpha_macs_per_s": alpha_macs / (avg["search"] * 1e-3),
-        "stats_gbs": stats_bytes / (avg["stats"] * 1e-3) / 1e9,
-        "pack_gbs": pack_bytes / (avg["pack"] * 1e-3) / 1e9,
-        "stats_gbs_cold": stats_bytes / (cold_ms["stats"] * 1e-3) / 1e9,
-        "pack_gbs_cold": pack_bytes / (cold_ms["pack"] * 1e-3) / 1e9,
+        "roofline": dict(core["roofline"], traffic=traffic_from_profile(spec.name)),
+        "stages_ms": core["stages_ms"],
+        "search_alpha_macs_per_s": core["search_alpha_macs_per_s"],
+        "stats_gbs": core["stats_gbs"],
+        "pack_gbs": core["pack_gbs"],
+        "stats_gbs_cold": core["stats_gbs_cold"],
+        "pack_gbs_cold": core["pack_gbs_cold"],
         "mfma_probe": probe,
-        "wall_ms_per_step": wall * 1e3 / args.steps,
-        "result": {"best_index": b, "best_alpha": b / grid if b >= 0 else None,
-                   "awq_mse": float(m[b]) if b >= 0 else None, "rtn_mse": float(m[0])},
+        "wall_ms_per_step": core["wall_ms_per_layer"],
+        "result": core["result"],
     }
     if not args.no_clip:
         rec["clip_search"] = clip_measure(awq, torch, spec, W, X, s_best, args)
@@ -557,6 +605,22 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         rec["copy_calib_bytes"] = src.numel()
+    if not args.no_configs:
+        # The other workloads: a few steps each (a config is a layer, its
+        # time scales with its alpha-candidate MACs), and the oracle's rate
+        # on a row sample of the same layer.
+        rec["configs"] = {}
+        for other in synth.CONFIGS:
+            if other.name == spec.name:
+                continue
+            n = 3 if other.alpha_macs > 1e12 else 10
+            c, tt = measure_layer(awq, torch, synth, other, n, 2, probe, cold_reps=3)
+            c["steps"] = n
+            if not args.no_cpu_baseline:
+                c["oracle"] = oracle_rate(other, tt["lay"], min(other.out, 64))
+            rec["configs"][other.name] = c
+            del tt
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], o = cpu_baseline(spec, lay, args.cpu_seconds)
         rec["parity"] = parity_record(awq, torch, spec, W, X, xmag, (m, b), o)
