@@ -28,9 +28,9 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 METRIC = "AWQ search: α-candidate·MACs/s + ms per layer (4096×4096, 256 tok, g128, 21 α)"
-SEARCH_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_search.hip")
+SEARCH_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_search16.hip")
 MFMA_PROBE = os.path.join(ROOT, "post_weight_quantization_30_amd", "mfma_peak")
-PMC_FILE = os.path.join(ROOT, "profiles", "k_search_linear_4096x4096_t256_hbm_counters.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "k_search16_linear_4096x4096_t256_hbm_counters.json")
 CLIP_SRC = os.path.join(ROOT, "post_weight_quantization_30_amd", "csrc", "k_clip.hip")
 CLIP_PMC_FILE = os.path.join(ROOT, "profiles", "k_clip_search_linear_4096x4096_t256_hbm_counters.json")
 
@@ -214,6 +214,9 @@ def fold_measure(awq, torch, spec, W, s_best, args):
     out, n_in = spec.out, spec.inn
     esize = W.element_size()
     buf = torch.empty_like(W)
+    # the producer has one output row per input channel of the layer
+    prod = W if out == n_in else torch.ones((n_in, out), dtype=W.dtype, device=W.device)
+    pbuf = buf if out == n_in else torch.empty_like(prod)
     gamma = torch.ones(n_in, dtype=W.dtype, device=W.device)
     gbuf = torch.empty_like(gamma)
 
@@ -230,7 +233,7 @@ def fold_measure(awq, torch, spec, W, s_best, args):
         return e0.elapsed_time(e1) / k
 
     k = max(args.clip_steps, 10)
-    rows_ms = timed(lambda: awq.fold_rows(W, s_best, out=buf), k)
+    rows_ms = timed(lambda: awq.fold_rows(prod, s_best, out=pbuf), k)
     cols_ms = timed(lambda: awq.scale_cols(W, s_best, out=buf), k)
     norm_ms = timed(lambda: awq.fold_rows(gamma, s_best, out=gbuf), k)
     nbytes = 2 * out * n_in * esize + 4 * n_in
