@@ -60,8 +60,14 @@ def parse():
 
 
 def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and blank lines left out, so a
+    comment edit does not orphan counters taken from the same code."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_from_profile(config, pmc_file=PMC_FILE, src=SEARCH_SRC):

@@ -14,26 +14,26 @@
 //    with v = w*s is built in registers and rounded once to the 16-bit
 //    operand type.
 //  * One block: 16 output rows x 256 tokens x up to 12 candidates, 8 waves
-//    (two per SIMD) of 32 tokens. The matrix instruction is
+//    (two per SIMD) of 64 tokens. The matrix instruction is
 //    v_mfma_f32_32x32x16: A = 32 tokens of X (shared by every candidate),
 //    B = the D rows of a PAIR of candidates (2 x 16 rows side by side in the
 //    32-wide N dimension), so a block's 16 rows still fill the instruction and
-//    each wave keeps 16 fp32 accumulators per candidate pair. The error is
-//    squared only after the full-K sum, so K is never split.
-//  * Measured on this GPU (mb_gfx950): a VALU wave next to an MFMA wave on
-//    one SIMD loses about 8 issue cycles per matrix instruction, i.e. half
-//    of a 16-cycle 16x16x32 but a quarter of a 32-cycle 32x32x16; and two
-//    waves per SIMD issue fp32 VALU work 1.2x faster than one. So every wave
-//    both runs its MFMAs for group g and builds D tiles for group g+1, with
-//    the two streams interleaved instruction by instruction
-//    (sched_group_barrier), instead of all waves alternating between an
-//    MFMA phase and a build phase.
+//    each wave keeps 16 fp32 accumulators per candidate pair and A tile. The
+//    error is squared only after the full-K sum, so K is never split.
+//  * Measured on this GPU (mb_gfx950): an MFMA-only wave keeps its rate
+//    next to a VALU wave on the same SIMD, which loses about 8 cycles per
+//    32x32x16 instruction. So every wave both runs its MFMAs for step si and
+//    builds D tiles for step si + 1, the two streams interleaved instruction
+//    by instruction in fenced slots (sched_barrier), instead of all waves
+//    alternating between an MFMA phase and a build phase.
 //  * Per step of 128 input columns (8 k-steps of 16; any group size that
 //    divides 128): the W tile (16 rows x 128) and the s and 1/s rows of the
-//    block's candidates go straight from global memory into LDS
-//    (global_load_lds_dwordx4), one step ahead; the D tiles are
-//    double-buffered in LDS in the exact lane layout of the B operand; one
-//    barrier per step.
+//    block's candidates are loaded into registers two steps ahead and
+//    written to LDS at the end of the step before they are built; the D
+//    tiles are double-buffered in LDS in the exact lane layout of the B
+//    operand; one barrier per step. X comes from a copy in matrix-fragment
+//    order (written by the preparation kernel below), so each A-fragment load
+//    is one contiguous 1 KB read.
 //  * D-tile building: a "unit" is one candidate's 16 x 128 tile, built by one
 //    wave, lane (r, c) = (lane & 15, lane >> 4) holding row r, columns
 //    32c .. 32c + 31. A block of n candidates has n units over 8 waves; the
