@@ -365,6 +365,327 @@ __global__ __launch_bounds__(kQWaves * 64) void k_qgemm(const TX *__restrict__ X
 }
 
 // ---------------------------------------------------------------------------
+// Decode, up to 4 tokens: a persistent grid (as many blocks as fit on the
+// chip at once), each block of 8 waves walking row tiles of 16 NT rows. A
+// row's codes are cut into batches of GPB consecutive groups (KB columns);
+// in each tile wave w takes batches w, w + 8, ... The block first copies the
+// M tokens of X into LDS, in the operand order of the code pairs; the MFMA
+// fragments are read from there (the lanes of tokens past M read token
+// M - 1: their products reach only accumulator rows that are never stored).
+// A wave's work is the list of (tile, batch) items; item i + 1 is loaded
+// into the other of two register sets while item i is computed, across tile
+// boundaries, so the codes of the next tile are in flight during the
+// reduction of the current one. Loads are whole-wave vector loads:
+//  * codes straight into registers: lane (r, c) takes quarter c of each group
+//    of row r (the k-slot order of the kernel above), so one instruction
+//    reads 16 rows x GB contiguous bytes and an item is 4 KB per row tile;
+//  * the row's GPB scales as one load and its GPB zeros as one (the layer
+//    has a whole number of batches per row, ng % GPB == 0, and the scale and
+//    zero arrays are aligned to GPB entries).
+// A tile ends with the waves' partial tiles added in wave order through LDS
+// (double-buffered: one barrier per tile).
+// ---------------------------------------------------------------------------
+template <int BITS, int G>
+struct DecBatch {
+    static constexpr int GB = G * BITS / 8;                     // bytes of one group of one row
+    static constexpr int QB = GB / 4;                           // bytes of a lane's quarter
+    static constexpr int WPL = QB / 4;                          // code words per lane per group
+    static constexpr int GPB = 4 * GB <= 256 ? 4 : 256 / GB;    // groups per batch
+};
+constexpr int kDecM = 4;                    // tokens
+constexpr int kDecXBytes = 64 * 1024;       // LDS for X: M (2 in + 16) bytes at most
+
+// The codes of one group of one lane as (code - zero) operands; the zero is
+// byte j of zw. fp16: a mask-and-or turns two codes 16 bits apart into the
+// fp16 pair 1024 + c (bits 0-3 of each half) or 1024 + 16 c (bits 4-7); one
+// packed fp16 subtraction of 1024 + zero, or fma with 1/16 and -(64 +
+// zero), leaves the exact small integers (every intermediate is exact).
+// Pairs come out in the order F16Pairs::PERM. With 4-bit codes (zero < 16)
+// both constants are bit patterns: 1024 + z is 0x6400 | z and -(64 + z) is
+// 0xD400 | z << 4, built from the zero byte copied into both halves.
+template <typename TX, int BITS, int G>
+__device__ __forceinline__ void dec_operands(const uint32_t *wv, uint32_t zw, int j,
+                                             typename QOp<TX>::vec (&b)[G / 32])
+{
+    constexpr int STEPS = G / 32;
+    constexpr uint32_t cmask = (1u << BITS) - 1u;
+    const int zero = (int)((zw >> (8 * j)) & 0xFFu);
+    if constexpr (std::is_same<TX, f16>::value && BITS == 4) {
+        // byte j of zw into bytes 0 and 2, zeros elsewhere (selector 0x0C)
+        const uint32_t zrep = __builtin_amdgcn_perm(zw, 0u, 0x0C000C00u | (uint32_t)(4 + j) << 16 | (uint32_t)(4 + j));
+        const f16x2 z1 = __builtin_bit_cast(f16x2, zrep | 0x64006400u);
+        const f16x2 z16 = __builtin_bit_cast(f16x2, (zrep << 4) | 0xD400D400u);
+        const f16x2 sixteenth = {static_cast<f16>(0.0625f), static_cast<f16>(0.0625f)};
+        const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = 0x64006400u;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            const uint32_t w = wv[s], w8 = w >> 8;
+            const f16x2 d0 = __builtin_bit_cast(f16x2, and_or(w, m_lo, magic)) - z1;
+            const f16x2 d1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, and_or(w, m_hi, magic)),
+                                                       sixteenth, z16);
+            const f16x2 d2 = __builtin_bit_cast(f16x2, and_or(w8, m_lo, magic)) - z1;
+            const f16x2 d3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, and_or(w8, m_hi, magic)),
+                                                       sixteenth, z16);
+            b[s][0] = d0[0]; b[s][1] = d0[1];
+            b[s][2] = d1[0]; b[s][3] = d1[1];
+            b[s][4] = d2[0]; b[s][5] = d2[1];
+            b[s][6] = d3[0]; b[s][7] = d3[1];
+        }
+    } else if constexpr (std::is_same<TX, f16>::value) {
+        const f16 zb = static_cast<f16>(1024 + zero);                  // exact: at most 1279
+        const f16x2 z2 = {zb, zb};
+        const uint32_t mask = F16Pairs<BITS>::kMask, magic = 0x64006400u;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            uint32_t u[4];
+            F16Pairs<BITS>::make(&wv[s * BITS / 4], u, mask, magic);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f16x2 d = __builtin_bit_cast(f16x2, u[p]) - z2;   // exact
+                b[s][2 * p] = d[0];
+                b[s][2 * p + 1] = d[1];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = 8 * s + e;
+                const int code = (int)((wv[(k * BITS) / 32] >> ((k * BITS) % 32)) & cmask);
+                b[s][e] = static_cast<TX>(static_cast<float>(code - zero));   // exact
+            }
+    }
+}
+
+template <int BITS, int G>
+struct DecRegs {
+    typedef DecBatch<BITS, G> D;
+    typedef float scv __attribute__((ext_vector_type(D::GPB)));
+    uint32_t wv[D::GPB][D::WPL];
+    scv sc;
+    uint32_t zw;                                                // GPB zero bytes
+};
+
+template <int BITS, int G>
+bool qgemv_applies(int64_t M, int64_t in, const float *scales, const uint8_t *zeros)
+{
+    typedef DecBatch<BITS, G> D;
+    return M <= kDecM && M * (2 * in + 16) <= kDecXBytes && (in / G) % D::GPB == 0 &&
+           ((uintptr_t)scales % (4 * D::GPB)) == 0 && ((uintptr_t)zeros % D::GPB) == 0;
+}
+
+template <typename TX, int BITS, int G, bool YF32>
+__global__ __launch_bounds__(kQWaves * 64) void k_qgemv(const TX *__restrict__ X, int64_t M, int64_t in,
+                                                        const uint32_t *__restrict__ qweight,
+                                                        const float *__restrict__ scales,
+                                                        const uint8_t *__restrict__ zeros, int64_t out,
+                                                        void *__restrict__ Y)
+{
+    typedef DecBatch<BITS, G> D;
+    typedef typename QOp<TX>::vec vec;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef DecRegs<BITS, G> R;
+    constexpr int STEPS = G / 32, GPB = D::GPB, WPL = D::WPL;
+    constexpr bool kPairs = std::is_same<TX, f16>::value;
+    extern __shared__ __align__(16) uint8_t dyn_lds[];          // X: M rows of 2 in + 16 bytes
+    __shared__ __align__(16) f32x4 red[2][kQWaves][16];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index as a scalar: the item bookkeeping and its branches are
+    // then uniform (scalar registers, no exec-masked paths)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, c = lane >> 4;
+    const int64_t ng = in / G, nb = ng / GPB;
+    const int64_t row_bytes = in * BITS / 8;
+    const int64_t ntiles = (out + 15) / 16;
+    const int64_t xrow = 2 * in + 16;
+    const uint8_t *qb = reinterpret_cast<const uint8_t *>(qweight);
+
+    // a wave's items: (tile, batch) for its tiles blockIdx.x + i gridDim.x
+    // and its batches wave + 8 j; the next item is the next batch of the
+    // tile or the first batch of the next tile
+    const int nw = nb < kQWaves ? (int)nb : kQWaves;            // waves with batches
+    auto advance = [&](int64_t &tile, int64_t &b) {
+        b += kQWaves;
+        if (b >= nb) {
+            b = wave;
+            tile += gridDim.x;
+        }
+    };
+
+    // Tile t covers rows base(t) .. base(t) + 15 with base(t) = 16 t, the last
+    // tile moved back to end at row out - 1 (it stores only rows past 16 t,
+    // the earlier ones belong to the tile before). A lane's offsets from the
+    // tile's first row are then the same in every tile: the per-item
+    // addresses are a scalar base plus these.
+    const int64_t last_base = out > 16 ? out - 16 : 0;
+    const int reff = out >= 16 ? r : (r < out ? r : (int)out - 1);
+    const uint32_t q_off = (uint32_t)(reff * row_bytes + c * D::QB);
+    const uint32_t s_off = (uint32_t)(reff * ng);
+    auto row_base = [&](int64_t tile) { return tile * 16 < last_base ? tile * 16 : last_base; };
+
+    auto fetch = [&](R &rg, int64_t tile, int64_t b) {
+        const int64_t g0 = b * GPB, n0 = row_base(tile);
+        const uint8_t *qrow = qb + n0 * row_bytes + g0 * D::GB + q_off;
+#pragma unroll
+        for (int j = 0; j < GPB; ++j) {
+            const uint8_t *src = qrow + j * D::GB;
+            if constexpr (WPL % 4 == 0) {
+#pragma unroll
+                for (int q = 0; q < WPL / 4; ++q) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 16 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        rg.wv[j][4 * q + e] = v[e];
+                }
+            } else if constexpr (WPL == 2) {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
+                rg.wv[j][0] = v[0];
+                rg.wv[j][1] = v[1];
+            } else {
+                rg.wv[j][0] = *reinterpret_cast<const uint32_t *>(src);
+            }
+        }
+        rg.sc = *reinterpret_cast<const typename R::scv *>(scales + n0 * ng + g0 + s_off);
+        if constexpr (GPB == 4)
+            rg.zw = *reinterpret_cast<const uint32_t *>(zeros + n0 * ng + g0 + s_off);
+        else
+            rg.zw = *reinterpret_cast<const uint16_t *>(zeros + n0 * ng + g0 + s_off);
+    };
+
+    const int mr = r < M ? r : (int)M - 1;
+    const uint8_t *xlane = dyn_lds + mr * xrow + c * (G / 4) * 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const R &cur, int64_t b) {
+        const uint8_t *xw = xlane + b * GPB * G * 2;
+#pragma unroll
+        for (int j = 0; j < GPB; ++j) {
+            vec xs[STEPS];
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s)
+                xs[s] = *reinterpret_cast<const vec *>(xw + (j * G + 8 * s) * 2);
+            vec bop[STEPS];
+            dec_operands<TX, BITS, G>(cur.wv[j], cur.zw, j, bop);
+            f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s)
+                part = QOp<TX>::mfma(xs[s], bop[s], part);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = fmaf(cur.sc[j], part[i], acc[i]);
+        }
+    };
+    // The end of a tile: the partial tiles to LDS, one barrier, wave 0 adds
+    // them in wave order and stores. Lane l, register i holds token
+    // 4 (l / 16) + i of row l % 16, so with at most 4 tokens only lanes 0-15
+    // hold results.
+    int par = 0;
+    auto tile_done = [&](int64_t tile) {
+        if (wave < nw && lane < 16)
+            red[par][wave][lane] = acc;
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        if (wave == 0 && lane < 16) {
+            f32x4 sum = red[par][0][lane];
+            for (int w = 1; w < nw; ++w)
+                sum += red[par][w][lane];
+            const int64_t nn = row_base(tile) + r;
+#pragma unroll
+            for (int i = 0; i < kDecM; ++i) {
+                if (i < M && nn < out && nn >= tile * 16) {
+                    if (YF32)
+                        static_cast<float *>(Y)[i * out + nn] = sum[i];
+                    else
+                        static_cast<TX *>(Y)[i * out + nn] = static_cast<TX>(sum[i]);
+                }
+            }
+        }
+        par ^= 1;
+    };
+
+    R ra, rb;
+    const bool busy = wave < nb;
+    if (busy)
+        fetch(ra, blockIdx.x, wave);                            // in flight while X is staged
+    // X into LDS: 16-byte pieces, permuted into the code pairs' order
+    for (int64_t p = tid; p < M * in / 8; p += kQWaves * 64) {
+        const int64_t m = p / (in / 8), k8 = p % (in / 8);
+        u32x4 v = *reinterpret_cast<const u32x4 *>(X + m * in + 8 * k8);
+        if constexpr (kPairs) {
+            constexpr const int *P = F16Pairs<BITS>::PERM;
+            const vec a = __builtin_bit_cast(vec, v);
+            v = __builtin_bit_cast(u32x4, __builtin_shufflevector(a, a, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
+                                                                  P[7]));
+        }
+        *reinterpret_cast<u32x4 *>(dyn_lds + m * xrow + 16 * k8) = v;
+    }
+    __syncthreads();
+    if (!busy) {
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
+            tile_done(tile);
+        return;
+    }
+    // The next item is loaded into the other register set while this one is
+    // computed. No copies between the sets (a copy would wait for the loads
+    // in flight), and the computation is repeated on the paths with and
+    // without a load behind it, so that each waits for its own item's loads
+    // only; the empty asm statements differ so that the compiler does not
+    // merge the two paths' last instructions after the join.
+    int64_t tile = blockIdx.x, b = wave;
+    int64_t ntile = tile, nbt = b;
+    advance(ntile, nbt);
+    while (true) {
+        if (ntile < ntiles) {
+            fetch(rb, ntile, nbt);
+            __builtin_amdgcn_sched_barrier(0);      // the loads go out before the computation
+            consume(ra, b);
+            asm volatile("; item a, next in flight" : "+v"(acc));
+        } else {
+            consume(ra, b);
+            asm volatile("; item a, last" : "+v"(acc));
+        }
+        if (ntile != tile)
+            tile_done(tile);
+        if (ntile >= ntiles)
+            break;
+        tile = ntile, b = nbt;
+        advance(ntile, nbt);
+        if (ntile < ntiles) {
+            fetch(ra, ntile, nbt);
+            __builtin_amdgcn_sched_barrier(0);      // the loads go out before the computation
+            consume(rb, b);
+            asm volatile("; item b, next in flight" : "+v"(acc));
+        } else {
+            consume(rb, b);
+            asm volatile("; item b, last" : "+v"(acc));
+        }
+        if (ntile != tile)
+            tile_done(tile);
+        if (ntile >= ntiles)
+            break;
+        tile = ntile, b = nbt;
+        advance(ntile, nbt);
+    }
+}
+
+// Blocks of the persistent decode grid: as many as fit on the device at once.
+template <typename K>
+static unsigned qgemv_grid(K kernel, size_t lds, int64_t ntiles)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kQWaves * 64, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1, cus = cus > 0 ? cus : 256;
+    // (measured: fewer blocks with an equal number of tiles each are slower
+    // than all that fit; the extra loads in flight outweigh the uneven tail)
+    const int64_t fit = (int64_t)cus * per_cu;
+    return (unsigned)(ntiles < fit ? ntiles : fit);
+}
+
+// ---------------------------------------------------------------------------
 // Prefill (many tokens): one block = 64 tokens x 128 output rows over all of
 // K, wave w taking rows 16 w .. +15 for all four 16-token tiles. K runs in
 // chunks of 128 columns: X (64 x 128) and the packed codes of the 128 rows
@@ -832,9 +1153,11 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
     // groups of 128 only (other widths and groups exceed the LDS or spill)
     constexpr bool kPf32x2 = BITS == 4 && G == 128;
     const bool pf32x2 = kPf32x2;
-    // decode (M <= 16): 16 tokens and 16 rows per block, or 32 rows on layers
-    // with at least 8192 rows (twice the bytes staged per round; enough blocks
-    // remain to fill the chip). Beyond 64 tokens, with in a multiple of 128,
+    // decode up to 4 tokens (whole batches per row, aligned scales and
+    // zeros): direct loads, 16 rows per block, or 32 on layers with at least
+    // 8192 rows. Otherwise up to 16 tokens: 16 tokens and 16 rows per block,
+    // or 32 rows on layers with at least 8192 rows (twice the bytes staged per
+    // round; enough blocks remain to fill the chip). Beyond 64 tokens, with in a multiple of 128,
     // the first prefill tile that gives at least one block per compute unit:
     // 32 x 32 MFMAs with 64 tokens x 512 rows (4-bit codes in groups of 128),
     // then 64 x 256, then the 16 x 16 tile with 64 x 128. Otherwise split
@@ -846,7 +1169,17 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
                        dim3((unsigned)((out + 16 * NT - 1) / (16 * NT)),                             \
                             (unsigned)((M + 16 * MT - 1) / (16 * MT))),                              \
                        block, 0, st, (const TX *)X, M, in, qweight, scales, zeros, out, Y)
-    if (M <= 16 && out < 8192) {
+#define AWQ_QGEMV(YF)                                                                                \
+    do {                                                                                             \
+        const size_t lds = (size_t)(M * (2 * in + 16));                                              \
+        auto k = k_qgemv<TX, BITS, G, YF>;                                                           \
+        hipLaunchKernelGGL(k, dim3(qgemv_grid(k, lds, (out + 15) / 16)), block, lds, st, (const TX *)X, M, in, \
+                           qweight, scales, zeros, out, Y);                                          \
+    } while (0)
+    const bool gemv = qgemv_applies<BITS, G>(M, in, scales, zeros);
+    if (gemv) {
+        if (yf32) AWQ_QGEMV(true); else AWQ_QGEMV(false);
+    } else if (M <= 16 && out < 8192) {
         if (yf32) AWQ_QGEMM(1, 1, true); else AWQ_QGEMM(1, 1, false);
     } else if (M <= 16) {
         if (yf32) AWQ_QGEMM(1, 2, true); else AWQ_QGEMM(1, 2, false);
@@ -884,6 +1217,7 @@ static hipError_t qgemm_mt(const void *X, int64_t M, int64_t in, const uint32_t 
                                scales, zeros, out, Y);
     }
 #undef AWQ_QGEMM
+#undef AWQ_QGEMV
     return hipGetLastError();
 }
 

@@ -101,6 +101,16 @@ CASES = [
     ("bf16", 8, 64, "asym", 1, 1, 64),          # a single output row and token
     ("f16", 4, 128, "asym", 3, 8200, 256),      # tall layer: 32-row decode blocks, ragged rows
     ("bf16", 8, 64, "sym", 16, 8192, 128),
+    # decode batches of four groups: a ragged last batch (5 groups), several
+    # batches per wave (in = 14336: 28 batches over 8 waves; 8-bit g32: 36)
+    ("f16", 4, 128, "asym", 4, 100, 640),
+    ("bf16", 4, 128, "sym", 8, 40, 14336),
+    ("f16", 8, 32, "sym", 1, 70, 4608),
+    # the persistent decode grid walking several row tiles per block (the
+    # register sets rotate across tile boundaries), the last tile moved back
+    ("f16", 4, 128, "asym", 1, 40000, 1024),
+    ("bf16", 4, 128, "sym", 2, 30001, 512),
+    ("f16", 8, 64, "asym", 3, 20007, 1024),
     # the 64-token x 128-row prefill tile (at least 256 blocks, in a multiple of 128)
     ("bf16", 4, 128, "sym", 1000, 4000, 256),    # ragged token and row tiles
     ("f16", 8, 64, "asym", 1100, 3900, 128),
