@@ -56,6 +56,9 @@ def parse():
                    help="skip the per-workload records of the other layers")
     p.add_argument("--clip-steps", type=int, default=10,
                    help="timed launches of the clipping-range search")
+    p.add_argument("--decode-only", action="store_true",
+                   help="only the decode product on the 28672 x 4096 int4 g128 layer, hot and cold "
+                        "(a short run for the profiler)")
     return p.parse_args()
 
 
@@ -252,83 +255,110 @@ def fold_measure(awq, torch, spec, W, s_best, args):
             "cols_gbs": nbytes / (cols_ms * 1e-3) / 1e9}
 
 
+def _graph_us(torch, launches, replays):
+    """Average time of one launch, from a HIP graph of the given launches
+    replayed back to back (the host's per-call overhead stays out)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in launches:
+            fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * len(launches))
+    del g
+    return us
+
+
+COLD_BYTES = 600 * 2 ** 20      # > 2x the 256 MB last-level cache
+
+
+def _decode_times(torch, awq, x, q, sc, z, bits, group, y, nbytes, replays):
+    """Decode time with the packed weights read hot (the same copy every
+    launch: after the first it is served from the last-level cache) and cold
+    (launches rotate over copies totalling more than twice that cache, so
+    every launch reads its weights from HBM). The cold one is the HBM figure."""
+    hot = _graph_us(torch, [lambda: awq.qgemm(x, q, sc, z, bits, group, y=y)] * 20, replays)
+    ncopy = max(2, COLD_BYTES // int(nbytes) + 1)
+    copies = [(q.clone(), sc.clone(), z.clone()) for _ in range(ncopy)]
+    cold = _graph_us(torch, [lambda c=c: awq.qgemm(x, c[0], c[1], c[2], bits, group, y=y) for c in copies],
+                     max(1, replays // 3))
+    del copies
+    return hot, cold, ncopy
+
+
 def qgemm_measure(awq, torch, spec, X, qweight, scales, zeros, s_best, args):
     """The deployment product over the layer's packed result: decode (1 and 16
     tokens, HBM-bound: the packed weights are read once), 256 tokens and a
     2048-token prefill (MFMA; the calibration tokens repeated). Launches are
     captured in a HIP graph so that the host's per-call overhead does not hide
-    the kernel time; the graph's result is checked against an eager call."""
+    the kernel time; the graph's result is checked against an eager call.
+    Decode is timed hot and cold (see _decode_times); its roofline uses the
+    cold time."""
     out, n_in = spec.out, spec.inn
     Xin = (X.float() / s_best[None, :]).to(X.dtype).contiguous()      # 1/s folded upstream
     res = {}
+    k = max(1, args.clip_steps // 2)
     for M in (1, 16, 256, 2048):
         xm = Xin.repeat((M + Xin.shape[0] - 1) // Xin.shape[0], 1)[:M].contiguous()
         y = torch.empty((M, out), dtype=X.dtype, device=X.device)
         awq.qgemm(xm, qweight, scales, zeros, spec.bits, spec.group, y=y)
         torch.cuda.synchronize()
         eager = y.clone()
-        reps = 20
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                awq.qgemm(xm, qweight, scales, zeros, spec.bits, spec.group, y=y)
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        k = max(1, args.clip_steps // 2)
-        e0.record()
-        for _ in range(k):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (k * reps)
-        if not torch.equal(y, eager):
-            raise RuntimeError("qgemm graph replay differs from the eager result")
         ng = n_in // spec.group
         nbytes = out * n_in * spec.bits / 8 + out * ng * 5 + M * n_in * 2 + M * out * 2
         flops = 2.0 * M * n_in * out
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        tfs = flops / (ms * 1e-3) / 1e12
+        rec = {}
         if M <= 16:
+            us, cold, ncopy = _decode_times(torch, awq, xm, qweight, scales, zeros, spec.bits, spec.group, y,
+                                            nbytes, k)
+            gbs = nbytes / cold / 1e3
+            rec = {"cold_us": cold, "cold_copies": ncopy, "hot_gbs": nbytes / us / 1e3}
             roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+                    "frac": gbs / PEAK_HBM_GBS, "traffic": None, "timing": "cold"}
         else:
+            us = _graph_us(torch, [lambda: awq.qgemm(xm, qweight, scales, zeros, spec.bits, spec.group, y=y)] * 20,
+                           k)
+            gbs = nbytes / us / 1e3
+            tfs = flops / us / 1e6
             roof = {"bound": "mfma", "achieved": tfs, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                     "frac": tfs / PEAK_F16_TFLOPS, "traffic": None}
-        res[f"M{M}"] = {"us": ms * 1e3, "bytes": nbytes, "gbs": gbs, "tflops": tfs, "roofline": roof}
-        del g
-    # decode on a wide layer (a gate/up-sized 28672 x 4096 int4 g128 stack,
-    # codes from a pack of seeded weights with s = 1): the transfer, not the
-    # launch and first round trip, dominates here
-    wo, wi, gw = 28672, 4096, 128
-    gen = torch.Generator(device=X.device).manual_seed(7)
-    Ww = (torch.randn((wo, wi), generator=gen, device=X.device) * 0.02).to(torch.float16)
-    qw, sw, zw = awq.quantize_pack(Ww, torch.ones(wi, dtype=torch.float32, device=X.device), 4, gw, "sym")
-    del Ww
-    xw = Xin[:1, :wi].to(torch.float16).contiguous()
-    yw = torch.empty((1, wo), dtype=torch.float16, device=X.device)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(20):
-            awq.qgemm(xw, qw, sw, zw, 4, gw, y=yw)
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 100
-    nbytes = wo * wi / 2 + wo * (wi // gw) * 5 + wi * 2 + wo * 2
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    res["M1_28672x4096"] = {"us": ms * 1e3, "bytes": nbytes, "gbs": gbs,
-                            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
-    del g
+        if not torch.equal(y, eager):
+            raise RuntimeError("qgemm graph replay differs from the eager result")
+        res[f"M{M}"] = {"us": us, "bytes": nbytes, "gbs": nbytes / us / 1e3, "tflops": flops / us / 1e6,
+                        **rec, "roofline": roof}
+    res["M1_28672x4096"] = wide_decode(awq, torch, Xin[:1, :4096].to(torch.float16).contiguous())
     return res
+
+
+def wide_decode(awq, torch, xw):
+    """Decode on a wide layer (a gate/up-sized 28672 x 4096 int4 g128 stack,
+    codes from a pack of seeded weights with s = 1): the transfer, not the
+    launch and first round trip, dominates here."""
+    wo, wi, gw = 28672, 4096, 128
+    gen = torch.Generator(device=xw.device).manual_seed(7)
+    Ww = (torch.randn((wo, wi), generator=gen, device=xw.device) * 0.02).to(torch.float16)
+    qw, sw, zw = awq.quantize_pack(Ww, torch.ones(wi, dtype=torch.float32, device=xw.device), 4, gw, "sym")
+    del Ww
+    yw = torch.empty((1, wo), dtype=torch.float16, device=xw.device)
+    nbytes = wo * wi / 2 + wo * (wi // gw) * 5 + wi * 2 + wo * 2
+    us, cold, ncopy = _decode_times(torch, awq, xw, qw, sw, zw, 4, gw, yw, nbytes, 5)
+    gbs = nbytes / cold / 1e3
+    return {"us": us, "cold_us": cold, "cold_copies": ncopy, "bytes": nbytes, "gbs": nbytes / us / 1e3,
+            "roofline": {"bound": "hbm", "kernel": "k_qgemv", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None, "timing": "cold"}}
+
+
+def decode_only(awq, torch):
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    xw = torch.randn((1, 4096), generator=gen, device="cuda").to(torch.float16)
+    return {"workload": "qgemm decode, 28672 x 4096 int4 g128, 1 token", **wide_decode(awq, torch, xw)}
 
 
 PEAK_F64_TFLOPS = 78.6          # MI355X fp64 matrix
@@ -558,6 +588,13 @@ def main():
               "(the row blocks are independent), which this measurement does not run.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.decode_only:
+        import torch
+        from post_weight_quantization_30_amd import awq
+        torch.cuda.set_device(0)
+        print(json.dumps(decode_only(awq, torch)), flush=True)
+        return
 
     probe = None if args.no_mfma_peak else measured_mfma_peak()
 
