@@ -433,6 +433,41 @@ def gptq_measure(awq, torch, spec, W, X, xmag_mse, args, awq_pack=None):
             "heldout_mse": held}
 
 
+def search_launch_cost(awq, torch, reps=10):
+    """The error kernel's fixed cost per launch: the search (fp16, int4 sym
+    g128, 21 candidates, 256 tokens) at 128 and 4096 input columns (1 and 32
+    pipeline steps of 128 columns) for 4096 and 2048 rows (two blocks per
+    compute unit and one). t(1 step) - (t(32) - t(1)) / 31 is what a launch
+    costs beyond its steps: block start-up (staging, the first tile build,
+    X prefetch), the epilogue and the launch itself. Seeded synthetic
+    layers (W ~ N(0, 0.02), X ~ N(0, 1))."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    res = {}
+    for out in (4096, 2048):
+        t = {}
+        for n_in in (128, 4096):
+            W = (torch.randn(out, n_in, device="cuda", generator=g) * 0.02).half()
+            X = torch.randn(256, n_in, device="cuda", generator=g).half()
+            xmag = awq.act_stats(X)
+            ws = torch.empty(awq.search_workspace_size(out, n_in, 256, 20), dtype=torch.uint8, device="cuda")
+            awq.search_prepare(X, xmag, out, 20, ws)
+            for _ in range(3):
+                awq.search_candidates(W, X, 4, 128, 20, "sym", ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                awq.search_candidates(W, X, 4, 128, 20, "sym", ws)
+            e1.record()
+            torch.cuda.synchronize()
+            t[n_in] = e0.elapsed_time(e1) * 1e3 / reps
+        step = (t[4096] - t[128]) / 31
+        res[f"out{out}"] = {"us_1_step": t[128], "us_32_steps": t[4096], "us_per_step": step,
+                            "us_fixed": t[128] - step, "blocks_per_cu": out // 16 * 2 // 256}
+    return res
+
+
 def measure_layer(awq, torch, synth, spec, steps, warmup, probe, cold_reps=5):
     """One workload: `steps` whole-path steps back to back (statistics, the
     single-call search, the pack), the same work again as separate stages with
@@ -638,6 +673,8 @@ def main():
     if not args.no_clip:
         rec["clip_search"] = clip_measure(awq, torch, spec, W, X, s_best, args)
     rec["fold"] = fold_measure(awq, torch, spec, W, s_best, args)
+    if spec.dtype == "f16":
+        rec["search_launch_cost"] = search_launch_cost(awq, torch)
     if spec.dtype in ("f16", "bf16") and spec.bits in (4, 8) and spec.group in (32, 64, 128):
         rec["qgemm"] = qgemm_measure(awq, torch, spec, X, qweight, scales, zeros, s_best, args)
     if not args.no_gptq:

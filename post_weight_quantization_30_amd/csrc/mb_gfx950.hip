@@ -23,6 +23,13 @@
 //    where the LDS read rate, not the matrix core, sets the pace.
 //  f64_latency: cycles per dependent v_fma_f64 (one chain per wave) and per
 //    independent one (8 chains).
+//  mfma_data: the matrix core's rate and the shader clock in the search
+//    kernel's launch shape (one 8-wave block per CU, two waves per SIMD,
+//    6 independent 32x32x16 f16 accumulators per wave), once with operands
+//    of random N(0, 1) fp16 values cycling over 4 A and 4 B fragments (the
+//    data an error contraction sees) and once with fixed small operands.
+//    The clock comes from the shader cycle counter (s_memtime) against the
+//    100 MHz real-time counter (s_memrealtime) over each wave's loop.
 //  layouts: the LDS placement of global_load_lds_dwordx4 (lane l's 16 bytes
 //    at the wave-uniform LDS address + 16 l) and the lane layouts of the A,
 //    B and C operands of
@@ -32,6 +39,7 @@
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <math.h>
 
 #include <algorithm>
 #include <vector>
@@ -338,6 +346,57 @@ __global__ void k_lds_dma(const float *src, float *dst)
         dst[i] = tgt[i];
 }
 
+// Matrix instructions on data: 24 v_mfma_f32_32x32x16_f16 per iteration over
+// 6 accumulators, A and B cycling over 4 register fragments each. RANDOM:
+// fragments loaded from src (random fp16); otherwise fixed small values.
+// rec per wave: shader cycles (2 words), real-time ticks (2 words).
+template <bool RANDOM>
+__global__ __launch_bounds__(kThreads, 1) void k_mfma_data(const f16x8 *__restrict__ src, uint32_t *rec,
+                                                           float *sink, int iters)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+    f16x8 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (RANDOM) {
+            a[i] = src[(w * 8 + i) * 64 + lane];
+            b[i] = src[(w * 8 + 4 + i) * 64 + lane];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                a[i][e] = (_Float16)(0.001f * (lane + e));
+                b[i][e] = (_Float16)(0.002f * (lane - e));
+            }
+        }
+    }
+    f32x16 acc[6];
+#pragma unroll
+    for (int c = 0; c < 6; ++c)
+        acc[c] = f32x16{};
+    __syncthreads();
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 24; ++j)
+            acc[j % 6] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j % 4], b[(j / 4 + j) % 4], acc[j % 6], 0, 0, 0);
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 6; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            sum += acc[c][e];
+    sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = sum;
+    if (lane == 0) {
+        rec[w * kRec + 0] = (uint32_t)(t1 - t0);
+        rec[w * kRec + 1] = (uint32_t)((t1 - t0) >> 32);
+        rec[w * kRec + 2] = (uint32_t)(r1 - r0);
+        rec[w * kRec + 3] = (uint32_t)((r1 - r0) >> 32);
+    }
+}
+
 static int g_cus = 0, g_clock_khz = 0;
 
 #define CHECK(x)                                                                          \
@@ -418,6 +477,47 @@ static void overlap_case(uint32_t *rec, float *sink, int iters, bool last)
            (m4.pairs_ok && sp.pairs_ok) ? "true" : "false", last ? "" : ",");
 }
 
+// One launch of k_mfma_data: median cycles per iteration, median clock,
+// matrix-core busy fraction per SIMD and the chip's TFLOP/s from event time.
+template <bool RANDOM>
+static void mfma_data_case(const f16x8 *src, uint32_t *rec, float *sink, int iters, bool last)
+{
+    const int nw = g_cus * (kThreads / 64);
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    hipLaunchKernelGGL(k_mfma_data<RANDOM>, dim3(g_cus), dim3(kThreads), kLdsPad, 0, src, rec, sink, iters);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(k_mfma_data<RANDOM>, dim3(g_cus), dim3(kThreads), kLdsPad, 0, src, rec, sink, iters);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    CHECK(hipEventDestroy(e0));
+    CHECK(hipEventDestroy(e1));
+    std::vector<uint32_t> h((size_t)nw * kRec);
+    CHECK(hipMemcpy(h.data(), rec, h.size() * 4, hipMemcpyDeviceToHost));
+    std::vector<double> cyc, ghz;
+    for (int w = 0; w < nw; ++w) {
+        const double c = (double)(((uint64_t)h[w * kRec + 1] << 32) | h[w * kRec + 0]);
+        const double r = (double)(((uint64_t)h[w * kRec + 3] << 32) | h[w * kRec + 2]);
+        cyc.push_back(c / iters);
+        if (r > 0)
+            ghz.push_back(c / r * 0.1);
+    }
+    std::sort(cyc.begin(), cyc.end());
+    std::sort(ghz.begin(), ghz.end());
+    const double c_med = cyc[cyc.size() / 2], g_med = ghz.empty() ? 0.0 : ghz[ghz.size() / 2];
+    // two waves per SIMD, 24 instructions of 32 cycles each per wave and iteration
+    const double busy = 2.0 * 24 * 32 / c_med;
+    const double flop = (double)nw * iters * 24 * (2.0 * 32 * 32 * 16);
+    printf("    \"%s\": {\"cycles_per_iter\": %.1f, \"clock_ghz\": %.3f, \"clock_ghz_min\": %.3f, "
+           "\"clock_ghz_max\": %.3f, \"matrix_busy\": %.3f, \"tflops\": %.1f}%s\n",
+           RANDOM ? "random_fp16" : "fixed_small", c_med, g_med, ghz.empty() ? 0.0 : ghz.front(),
+           ghz.empty() ? 0.0 : ghz.back(), busy, flop / (ms * 1e-3) / 1e12, last ? "" : ",");
+}
+
 int main()
 {
     int dev = 0;
@@ -479,6 +579,30 @@ int main()
                "\"same_addr_bytes_per_cu_clk\": %.1f},\n",
                r0.cyc_active, r1.cyc_active, r2.cyc_active, 65536.0 / r0.cyc_active,
                65536.0 / r1.cyc_active, 65536.0 / r2.cyc_active);
+    }
+    {
+        // random fp16 operands, 8 fragments of 64 lanes x 8 values per wave
+        const size_t n = (size_t)g_cus * (kThreads / 64) * 8 * 64 * 8;
+        std::vector<_Float16> hsrc(n);
+        uint64_t x = 0x9e3779b97f4a7c15ull;
+        for (size_t i = 0; i < n; i += 2) {
+            // Box-Muller on a 64-bit xorshift stream
+            x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+            const double u1 = ((x >> 11) + 1.0) / 9007199254740993.0;
+            x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+            const double u2 = (x >> 11) / 9007199254740992.0;
+            const double rr = sqrt(-2.0 * log(u1));
+            hsrc[i] = (_Float16)(rr * cos(6.283185307179586 * u2));
+            hsrc[i + 1] = (_Float16)(rr * sin(6.283185307179586 * u2));
+        }
+        f16x8 *src = nullptr;
+        CHECK(hipMalloc(&src, n * sizeof(_Float16)));
+        CHECK(hipMemcpy(src, hsrc.data(), n * sizeof(_Float16), hipMemcpyHostToDevice));
+        printf("  \"mfma_data\": {\n");
+        mfma_data_case<true>(src, rec, sink, iters, false);
+        mfma_data_case<false>(src, rec, sink, iters, true);
+        printf("  },\n");
+        CHECK(hipFree(src));
     }
     {
         const Result d1 = run(k_f64<1>, rec, sink, iters);
