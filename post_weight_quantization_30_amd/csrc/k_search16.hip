@@ -43,8 +43,9 @@
 //    (lane >> 5) covers columns 64h + 8s .. 64h + 8s + 7 for both A and B (a
 //    contraction may permute k), so every lane's X and D fragments are
 //    contiguous 128-byte runs.
-//  * Epilogue: squares in fp64, fixed butterflies, fixed-order sum over the
-//    waves; no atomics, bitwise reproducible.
+//  * Epilogue: each lane's squares summed in fp32 fused multiply-adds, then
+//    fp64 fixed butterflies and a fixed-order sum over the waves; no
+//    atomics, bitwise reproducible.
 //  * The search may round differently from the exact quantizer (reciprocal
 //    multiply, 16-bit D): only the error is produced here, and its tolerance
 //    allows that. Stored codes come from the exact kernel in k_pack.hip.
@@ -189,6 +190,33 @@ __device__ __forceinline__ float min3(float a, float b, float c)
     float r;
     asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
     return r;
+}
+
+// Sum of an fp64 value over the 16 lanes of each row and the two halves of
+// the wave, in registers: each step adds the value of a partner lane (DPP
+// quad_perm swaps of 1 and 2 lanes, row_half_mirror and row_mirror, which
+// after the steps before pair lanes holding the sums of different quarters
+// and halves of the row, then permlane32_swap across the halves); every
+// lane ends with the same total, bitwise the xor butterfly's since each step
+// adds the same two partial sums.
+template <int CTRL> __device__ __forceinline__ double dpp_f64(double x)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, (uint64_t)hi << 32 | lo);
+}
+__device__ __forceinline__ double wave_rows_sum_f64(double x)
+{
+    x += dpp_f64<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_f64<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_f64<0x141>(x);   // row_half_mirror
+    x += dpp_f64<0x140>(x);   // row_mirror
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    return __builtin_bit_cast(double, (uint64_t)(uint32_t)hi[0] << 32 | (uint32_t)lo[0]) +
+           __builtin_bit_cast(double, (uint64_t)(uint32_t)hi[1] << 32 | (uint32_t)lo[1]);
 }
 
 template <typename T> __device__ __forceinline__ typename Vec8<T>::type pack8(const float *d);
@@ -498,16 +526,6 @@ struct Search {
                          : reinterpret_cast<u32x4 *>(&sm.st[par][which][2 * m][0]) + lane;
         };
 
-        // Empty slots (an odd count, or pairs past the candidates) hold zero
-        // tiles in both buffers; nobody builds them.
-        for (int e = threadIdx.x; e < 2 * kPairs * kKs * 64; e += kWaves * 64) {
-            const int b = e / (kPairs * kKs * 64), p = (e / (kKs * 64)) % kPairs;
-            const int ln = e % 64;
-            const int slot = 2 * p + ((ln & 31) >> 4);
-            if (slot >= na)
-                sm.d[b][p][(e / 64) % kKs][ln] = V8{};
-        }
-
         f32x16 acc[NPW][2];
 #pragma unroll
         for (int p = 0; p < NPW; ++p)
@@ -530,19 +548,40 @@ struct Search {
             unit_init_p(un, i, &sm.st[sb][0][0][0], &sm.w[sb][0][0], &sm.d[dp][0][0][0]);
         };
 
-        // Prologue: stage steps 0 and 1, build step 0 (plainly), load X of
-        // the first kXr k-steps.
+        // Prologue: the loads staging steps 0 and 1 and those of X for the
+        // first kXr k-steps go out first; the zero tiles are written while
+        // they are in flight; then the staged data goes to LDS and step 0 is
+        // built (plainly).
+        u32x4 pre[kStg][2];
 #pragma unroll
         for (int i = 0; i < kStg; ++i) {
             const int64_t si = i < nsteps ? i : slast;
-            const u32x4 a = *stage_src(si, 0), b2 = *stage_src(si, 1);
-            *stage_dst(i, 0) = a;
-            *stage_dst(i, 1) = b2;
+            pre[i][0] = *stage_src(si, 0);
+            pre[i][1] = *stage_src(si, 1);
         }
 #pragma unroll
         for (int s = 0; s < kXr; ++s) {
             xr[s][0] = load8(xp0 + s * 512);
             xr[s][1] = load8(xp1 + s * 512);
+        }
+        // Empty slots (an odd count, or pairs past the candidates) hold zero
+        // tiles in both buffers; nobody builds them. Pairs below na / 2 are
+        // full, so only the pairs from there on are visited.
+        {
+            const int p0 = na >> 1, np = kPairs - p0;
+            for (int e = threadIdx.x; e < 2 * np * kKs * 64; e += kWaves * 64) {
+                const int b = e / (np * kKs * 64), p = p0 + (e / (kKs * 64)) % np;
+                const int ln = e % 64;
+                const int slot = 2 * p + ((ln & 31) >> 4);
+                if (slot >= na)
+                    sm.d[b][p][(e / 64) % kKs][ln] = V8{};
+            }
+        }
+
+#pragma unroll
+        for (int i = 0; i < kStg; ++i) {
+            *stage_dst(i, 0) = pre[i][0];
+            *stage_dst(i, 1) = pre[i][1];
         }
         __syncthreads();
 #pragma unroll
@@ -629,26 +668,33 @@ struct Search {
         // n = l & 31 of the C tile -- candidate slot 2 (pair0 + p) + (n >> 4),
         // row n & 15 -- and tokens 32t + 8(e/4) + 4(l >> 5) + (e & 3),
         // e = 0..15, of the wave's 64. Entries of rows or tokens past the end
-        // are left out.
+        // are left out. A lane's squares are summed in fp32, two chains of 16
+        // fused multiply-adds (one per A tile, relative rounding below 1e-6),
+        // added in fp64; the sums across lanes, waves and blocks are fp64.
         const int n = lane & 31;
         const bool row_ok = rb * kRows + (n & 15) < out;
+        const bool full = tok0 + 2 * kTokW <= tokens;   // every token of the wave exists
 #pragma unroll
         for (int p = 0; p < NPW; ++p) {
-            double sum = 0.0;
+            float s2[2] = {0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                if (full) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t tk = tok0 + 32 * t + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    const double x = row_ok && tk < tokens ? (double)acc[p][t][e] : 0.0;
-                    sum += x * x;
+                    for (int e = 0; e < 16; ++e)
+                        s2[t] = fmaf(acc[p][t][e], acc[p][t][e], s2[t]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int64_t tk = tok0 + 32 * t + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const float x = tk < tokens ? acc[p][t][e] : 0.f;
+                        s2[t] = fmaf(x, x, s2[t]);
+                    }
                 }
-            // lanes with the same slot: xor 1, 2, 4, 8 (inside 16) and 32
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
-            sum += __shfl_xor(sum, 4);
-            sum += __shfl_xor(sum, 8);
-            sum += __shfl_xor(sum, 32);
+            }
+            double sum = row_ok ? (double)s2[0] + (double)s2[1] : 0.0;
+            // lanes with the same slot: the 16 of each row and both halves
+            sum = wave_rows_sum_f64(sum);
             if (lane == 0)
                 sm.wsum[g][2 * (pair0 + p)] = sum;
             if (lane == 16)
@@ -725,8 +771,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_search16(
     int uslot[2];
     uslot[0] = (wave - u0 + na) % na;
     uslot[1] = (ub - u0 + na) % na;
-    // Exact arithmetic for units whose scales are all ones.
-    const bool ex = unit[a0 + uslot[0]] != 0 || (nunits == 2 && unit[a0 + uslot[1]] != 0);
+    // Exact arithmetic for units whose scales are all ones. Both flags are
+    // read (uslot[1] < na always), so the two loads share one round trip.
+    const int32_t f0 = unit[a0 + uslot[0]], f1 = unit[a0 + uslot[1]];
+    const bool ex = f0 != 0 || (nunits == 2 && f1 != 0);
     const int64_t nblk = nrb * ntb;
     const int64_t blk = k.rb * ntb + k.tb;
     typedef Search<T, G, ASYM> S;
