@@ -47,6 +47,8 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run a plain device copy of known size (HBM counter calibration)")
+    p.add_argument("--no-launch-cost", action="store_true",
+                   help="skip the search kernel's launch-cost record (other shapes of the same kernel)")
     p.add_argument("--no-mfma-peak", action="store_true",
                    help="skip the attainable-MFMA-peak probe")
     p.add_argument("--no-clip", action="store_true",
@@ -673,7 +675,7 @@ def main():
     if not args.no_clip:
         rec["clip_search"] = clip_measure(awq, torch, spec, W, X, s_best, args)
     rec["fold"] = fold_measure(awq, torch, spec, W, s_best, args)
-    if spec.dtype == "f16":
+    if spec.dtype == "f16" and not args.no_launch_cost:
         rec["search_launch_cost"] = search_launch_cost(awq, torch)
     if spec.dtype in ("f16", "bf16") and spec.bits in (4, 8) and spec.group in (32, 64, 128):
         rec["qgemm"] = qgemm_measure(awq, torch, spec, X, qweight, scales, zeros, s_best, args)
