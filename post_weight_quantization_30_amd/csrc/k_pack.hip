@@ -73,18 +73,41 @@ __device__ __forceinline__ float div_rn(float a, float b, float y)
 // rne(lo / scale) = -zero for asymmetric ones (rne is odd and monotone), so
 // FAST drops the other clamps. (Codes of groups with NaN values are
 // unspecified.)
+//
+// FAST first rounds u = v * y (y = RN(1/scale)): u lies within
+// 1.5 * 2^-23 |v / scale| <= 1.5 * 2^(BITS-23) of the correctly rounded
+// quotient (|v / scale| <= 2^BITS here), so rne(u) is rne of that quotient
+// unless u lies within that distance of a half-integer (a tie included). A
+// wave in which some u lies within 2^(BITS-21) of one computes all its
+// quotients correctly rounded instead (rare: about 2^(BITS-20) of the
+// weights are that close).
 template <int BITS, bool ASYM, bool FAST>
 __device__ __forceinline__ void codes(const float (&v)[32], float scale, float lo, float hi, float zero,
                                       uint32_t (&word)[BITS])
 {
     const float y = FAST ? 1.0f / scale : 0.0f;
+    float qs[32];
+    if (FAST) {
+        float dmax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float u = v[i] * y;
+            qs[i] = rintf(u);
+            dmax = fmaxf(dmax, fabsf(u - qs[i]));
+        }
+        const float thr = 0.5f - (float)(1 << BITS) * 0x1p-21f;
+        if (__builtin_amdgcn_ballot_w64(dmax >= thr) != 0) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                qs[i] = rintf(div_rn(v[i], scale, y));
+        }
+    }
 #pragma unroll
     for (int k = 0; k < BITS; ++k)
         word[k] = 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const float u = FAST ? div_rn(v[i], scale, y) : v[i] / scale;
-        float q = rintf(u);
+        float q = FAST ? qs[i] : rintf(v[i] / scale);
         uint32_t code;
         if (ASYM) {
             q = FAST ? fminf(q + zero, hi) : fminf(fmaxf(q + zero, lo), hi);
@@ -125,6 +148,19 @@ __global__ __launch_bounds__(kPackRows * 64) void k_quantize_pack(const T *__res
     const int64_t tiles = (chunks + kPackChunks - 1) / kPackChunks;
     const int64_t rblk = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row_raw = rblk * kPackRows + wave, ch_raw = tile * kPackChunks + lane;
+    const bool active = row_raw < out && ch_raw < chunks;
+    const int64_t row = active ? row_raw : 0;
+    const int64_t ch = active ? ch_raw : 0;
+    // the lane's 32 weights, loaded before the scale factors' staging and
+    // barrier so that the two memory round trips overlap
+    typename Vec8<T>::type wl[4];
+    {
+        const T *wp = W + row * in + ch * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            wl[q] = load8(wp + q * 8);
+    }
     {
         const int l = threadIdx.x >> 2, part = threadIdx.x & 3;   // 8 factors each
         const int64_t col = (tile * kPackChunks + l) * 32 + part * 8;
@@ -135,21 +171,16 @@ __global__ __launch_bounds__(kPackRows * 64) void k_quantize_pack(const T *__res
         sl[2 * part + 1][l] = f32x4v{s8[4], s8[5], s8[6], s8[7]};
     }
     __syncthreads();
-    const int64_t row_raw = rblk * kPackRows + wave, ch_raw = tile * kPackChunks + lane;
-    const bool active = row_raw < out && ch_raw < chunks;
-    const int64_t row = active ? row_raw : 0;
-    const int64_t ch = active ? ch_raw : 0;
 
     float v[32];
     if (active) {
-        const T *wp = W + row * in + ch * 32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const f32x4v s_lo = sl[2 * q][lane], s_hi = sl[2 * q + 1][lane];
             const f32x8 s8 = {s_lo[0], s_lo[1], s_lo[2], s_lo[3], s_hi[0], s_hi[1], s_hi[2], s_hi[3]};
             if constexpr (std::is_same<T, f16>::value) {
                 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                const u32x4 pr = __builtin_bit_cast(u32x4, load8(wp + q * 8));
+                const u32x4 pr = __builtin_bit_cast(u32x4, wl[q]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[q * 8 + 2 * e] = mul_f16_exact<0>(pr[e], s8[2 * e]);
@@ -157,7 +188,7 @@ __global__ __launch_bounds__(kPackRows * 64) void k_quantize_pack(const T *__res
                 }
             } else {
                 float w8[8];
-                widen8<T>(load8(wp + q * 8), w8);
+                widen8<T>(wl[q], w8);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     v[q * 8 + i] = w8[i] * s8[i];
