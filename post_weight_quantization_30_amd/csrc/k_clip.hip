@@ -320,6 +320,7 @@ __global__ __launch_bounds__(kClipThreads, 2) void k_clip_search(
     imax = clip_lanes4_max(imax);
     const float levels = (float)((1 << (bits - 1)) - 1);
     const float maxq = (float)((1 << bits) - 1);
+    const float qthr = 0.5f - ldexpf(1.0f, bits - 21);
 
     // Power-of-two scale of the row's D (fp16 parts only): 2^k |d| < 2^14,
     // and 2^k / s stays finite.
@@ -382,11 +383,28 @@ __global__ __launch_bounds__(kClipThreads, 2) void k_clip_search(
 #pragma unroll
             for (int m = 0; m < RW; ++m) {
                 if (m < nv) {
+                    // rne of the correctly rounded quotient x / scale: from
+                    // x * y, unless some lane's x * y lies within
+                    // 2^(bits-21) of a half-integer (|x / scale| <= 2^bits;
+                    // x * y lies within 1.5 * 2^(bits-23) of the quotient),
+                    // in which case the wave takes the two residual steps
+                    float xq[8], qq[8], dmax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        xq[e] = __builtin_amdgcn_fmed3f(v[e], xlo[m], xhi[m]);
+                        const float u = xq[e] * y[m];
+                        qq[e] = rintf(u);
+                        dmax = fmaxf(dmax, fabsf(u - qq[e]));
+                    }
+                    if (__builtin_amdgcn_ballot_w64(dmax >= qthr) != 0) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            qq[e] = rintf(clip_div(xq[e], scale[m], y[m]));
+                    }
                     float d[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float x = __builtin_amdgcn_fmed3f(v[e], xlo[m], xhi[m]);
-                        float q = rintf(clip_div(x, scale[m], y[m]));
+                        float q = qq[e];
                         float wh;
                         if (!ASYM) {
                             // |x| <= mx and scale >= RN(mx / levels) give
