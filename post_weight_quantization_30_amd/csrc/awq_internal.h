@@ -168,8 +168,20 @@ __device__ __forceinline__ void finish_block(const double *__restrict__ partial,
     const int nwaves = blockDim.x >> 6;
     for (int a = wave; a < n_alpha; a += nwaves) {
         const double *p = partial + (int64_t)a * nblk;
+        // lane l adds partials l, l + 64, l + 128, ... in that order; the
+        // loads of 16 (then 4) of them go out before their adds, so a long
+        // list costs one memory round trip per 16 partials of a lane
         double acc = 0.0;
         int64_t b = lane;
+        for (; b + 15 * 64 < nblk; b += 16 * 64) {
+            double x[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                x[u] = p[b + 64 * u];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                acc += x[u];
+        }
         for (; b + 192 < nblk; b += 256) {
             const double x0 = p[b], x1 = p[b + 64], x2 = p[b + 128], x3 = p[b + 192];
             acc += x0;
@@ -203,16 +215,16 @@ __device__ __forceinline__ void finish_block(const double *__restrict__ partial,
     __syncthreads();
     const int bi = *sbest;
     const float *src = s_tab + (int64_t)(bi >= 0 ? bi : 0) * in;
-    // four independent loads in flight per thread per round
-    for (int64_t j0 = threadIdx.x; j0 < in; j0 += 4 * (int64_t)blockDim.x) {
-        float x[4];
+    // sixteen independent loads in flight per thread per round
+    for (int64_t j0 = threadIdx.x; j0 < in; j0 += 16 * (int64_t)blockDim.x) {
+        float x[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 16; ++u) {
             const int64_t j = j0 + u * (int64_t)blockDim.x;
             x[u] = bi >= 0 && j < in ? src[j] : 1.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 16; ++u) {
             const int64_t j = j0 + u * (int64_t)blockDim.x;
             if (j < in)
                 s_best[j] = x[u];
